@@ -1,0 +1,258 @@
+// C ABI of libfgg.so: argument validation, device check and dispatch to the
+// kernels.  Every entry point either returns an error before launching
+// anything or enqueues its kernels on the caller's stream and returns.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+
+#include "../../include/fgg.h"
+#include "fgg_internal.hpp"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+std::atomic<int> g_num_cus_override{0};
+
+constexpr int kMaxDevices = 64;
+struct DeviceInfo {
+  std::once_flag once;
+  bool gfx950 = false;
+  int num_cus = 0;
+};
+DeviceInfo g_dev[kMaxDevices];
+
+bool debug_enabled() {
+  static const bool on = [] {
+    const char* e = std::getenv("FGG_DEBUG");
+    return e != nullptr && e[0] != '\0' && e[0] != '0';
+  }();
+  return on;
+}
+
+fgg_status hip_fail(hipError_t e) {
+  g_last_hip_error = (int)e;
+  return FGG_ERR_HIP;
+}
+
+// Current device must be gfx950; fills num_cus.
+fgg_status device_check(int* num_cus) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e);
+  if (dev < 0 || dev >= kMaxDevices) return FGG_ERR_UNSUPPORTED;
+  DeviceInfo& d = g_dev[dev];
+  std::call_once(d.once, [&] {
+    hipDeviceProp_t p;
+    if (hipGetDeviceProperties(&p, dev) != hipSuccess) return;
+    d.gfx950 = std::strncmp(p.gcnArchName, "gfx950", 6) == 0;
+    d.num_cus = p.multiProcessorCount;
+  });
+  if (!d.gfx950) return FGG_ERR_UNSUPPORTED;
+  const int ov = g_num_cus_override.load();
+  if (num_cus) *num_cus = ov > 0 ? ov : d.num_cus;
+  return FGG_OK;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool same_q(const fgg_qdesc& q, fgg_dtype data, fgg_dtype scale, int br, int bk) {
+  return q.data == data && q.scale == scale && q.block_rows == br && q.block_k == bk;
+}
+
+fgg_status finish(hipError_t e) { return e == hipSuccess ? FGG_OK : hip_fail(e); }
+
+}  // namespace
+
+extern "C" {
+
+const char* fgg_status_string(fgg_status s) {
+  switch (s) {
+    case FGG_OK: return "FGG_OK";
+    case FGG_ERR_INVALID_VALUE: return "FGG_ERR_INVALID_VALUE";
+    case FGG_ERR_UNSUPPORTED: return "FGG_ERR_UNSUPPORTED";
+    case FGG_ERR_HIP: return "FGG_ERR_HIP";
+  }
+  return "FGG_ERR_UNKNOWN";
+}
+
+int fgg_last_hip_error(void) { return g_last_hip_error; }
+
+fgg_status fgg_set_num_cus(int n) {
+  if (n < 0) return FGG_ERR_INVALID_VALUE;
+  g_num_cus_override.store(n);
+  return FGG_OK;
+}
+
+fgg_status fgg_quantize_blockwise(const void* x, fgg_dtype x_dtype, int64_t rows, int64_t cols, int64_t ldx,
+                                  fgg_act act, fgg_qdesc q, void* q_out, void* scales_out, void* stream) {
+  if (rows < 0 || cols < 0) return FGG_ERR_INVALID_VALUE;
+  if (x_dtype != FGG_F32 && x_dtype != FGG_BF16) return FGG_ERR_UNSUPPORTED;
+  if (act != FGG_ACT_NONE && act != FGG_ACT_SILU_MUL) return FGG_ERR_INVALID_VALUE;
+  fgg::QuantKind kind;
+  if (same_q(q, FGG_E4M3, FGG_F32, 1, 128)) kind = fgg::QuantKind::E4M3_1x128;
+  else if (same_q(q, FGG_E4M3, FGG_F32, 128, 128)) kind = fgg::QuantKind::E4M3_128x128;
+  else if (same_q(q, FGG_E2M1X2, FGG_F32, 1, 16)) kind = fgg::QuantKind::E2M1_1x16;
+  else if (same_q(q, FGG_E2M1X2, FGG_E8M0, 1, 32)) kind = fgg::QuantKind::E2M1_E8M0_1x32;
+  else return FGG_ERR_UNSUPPORTED;
+  const bool silu = act == FGG_ACT_SILU_MUL;
+  if (silu && kind != fgg::QuantKind::E4M3_1x128) return FGG_ERR_UNSUPPORTED;
+  if (cols % q.block_k != 0) return FGG_ERR_UNSUPPORTED;
+  if (q.block_rows == 128 && rows % 128 != 0) return FGG_ERR_UNSUPPORTED;
+  if (rows == 0 || cols == 0) return FGG_OK;
+  if (!x || !q_out || !scales_out) return FGG_ERR_INVALID_VALUE;
+  const int64_t need = silu ? 2 * cols : cols;
+  if (ldx < need) return FGG_ERR_INVALID_VALUE;
+  const int64_t esz = x_dtype == FGG_F32 ? 4 : 2;
+  if (!aligned(x, 16) || (ldx * esz) % 16 != 0 || !aligned(q_out, 16) || !aligned(scales_out, 4))
+    return FGG_ERR_INVALID_VALUE;
+  fgg_status st = device_check(nullptr);
+  if (st != FGG_OK) return st;
+  return finish(fgg::launch_quantize(x, x_dtype == FGG_BF16, rows, cols, ldx, kind, silu, q_out, scales_out,
+                                     (hipStream_t)stream));
+}
+
+fgg_status fgg_moe_permute_workspace(int64_t T, int32_t k, int32_t E, size_t* bytes) {
+  if (!bytes || T < 0 || k < 1 || k > 64 || E < 1 || E > 1024) return FGG_ERR_INVALID_VALUE;
+  *bytes = fgg::permute_workspace_bytes(T, k, E);
+  return FGG_OK;
+}
+
+fgg_status fgg_moe_permute(const int32_t* topk_ids, int64_t T, int32_t k, int32_t E, int32_t align,
+                           const void* xq, const float* xs, int64_t K, int32_t* offsets, int32_t* counts,
+                           int32_t* src_to_row, int32_t* row_to_src, void* a_out, float* sa_out,
+                           int64_t M_cap, void* workspace, size_t ws_bytes, void* stream) {
+  if (T < 0 || k < 1 || k > 64 || E < 1 || E > 1024 || align < 1 || align > 1024 || M_cap < 0)
+    return FGG_ERR_INVALID_VALUE;
+  if (!offsets || !counts) return FGG_ERR_INVALID_VALUE;
+  if (T > 0 && (!topk_ids || !src_to_row)) return FGG_ERR_INVALID_VALUE;
+  if (M_cap > 0 && !row_to_src) return FGG_ERR_INVALID_VALUE;
+  if (T * (int64_t)k > (int64_t)INT32_MAX || M_cap > (int64_t)INT32_MAX) return FGG_ERR_UNSUPPORTED;
+  if (xq) {
+    if (K <= 0 || K % 128 != 0) return FGG_ERR_UNSUPPORTED;
+    if (!xs || !a_out || !sa_out) return FGG_ERR_INVALID_VALUE;
+    if (!aligned(xq, 16) || !aligned(a_out, 16) || !aligned(xs, 4) || !aligned(sa_out, 4))
+      return FGG_ERR_INVALID_VALUE;
+  }
+  if (T > 0 && (!workspace || ws_bytes < fgg::permute_workspace_bytes(T, k, E))) return FGG_ERR_INVALID_VALUE;
+  fgg_status st = device_check(nullptr);
+  if (st != FGG_OK) return st;
+  return finish(fgg::launch_permute(topk_ids, T, k, E, align, (const uint8_t*)xq, xs, K, offsets, counts,
+                                    src_to_row, row_to_src, (uint8_t*)a_out, sa_out, M_cap, workspace,
+                                    (hipStream_t)stream));
+}
+
+fgg_status fgg_grouped_gemm_scaled(fgg_layout layout, int32_t G, int64_t M, int64_t N, int64_t K,
+                                   const void* a, const void* a_scales, fgg_qdesc aq, const void* b,
+                                   const void* b_scales, fgg_qdesc bq, const int32_t* offsets,
+                                   const int32_t* masked_m, void* d, int64_t ldd, void* stream) {
+  if (G < 1 || G > 1024 || M < 0 || N < 0 || K < 0) return FGG_ERR_INVALID_VALUE;
+  if (N % 128 != 0 || K % 128 != 0) return FGG_ERR_UNSUPPORTED;
+  if (ldd < N || ldd % 8 != 0) return FGG_ERR_INVALID_VALUE;
+  if (!same_q(aq, FGG_E4M3, FGG_F32, 1, 128)) return FGG_ERR_UNSUPPORTED;
+  if (!a || !a_scales || !b || !b_scales || !d) return FGG_ERR_INVALID_VALUE;
+  if (!aligned(a, 16) || !aligned(b, 16) || !aligned(d, 16) || !aligned(a_scales, 4) || !aligned(b_scales, 4))
+    return FGG_ERR_INVALID_VALUE;
+  int num_cus = 0;
+  if (layout == FGG_LAYOUT_CONTIGUOUS) {
+    if (!same_q(bq, FGG_E4M3, FGG_F32, 128, 128)) return FGG_ERR_UNSUPPORTED;
+    if (!offsets) return FGG_ERR_INVALID_VALUE;
+    fgg_status st = device_check(&num_cus);
+    if (st != FGG_OK) return st;
+    if (debug_enabled())
+      std::fprintf(stderr, "[fgg] grouped_gemm contiguous G=%d M=%lld N=%lld K=%lld tile=128x128x128 stages=2 lds=%d B grid<=%d\n",
+                   G, (long long)M, (long long)N, (long long)K, 2 * (128 * 128 * 2 + 512), num_cus * 2);
+    if (M == 0 || N == 0) return FGG_OK;
+    return finish(fgg::launch_gemm_fp8_contig(G, M, N, K, (const uint8_t*)a, (const float*)a_scales,
+                                              (const uint8_t*)b, (const float*)b_scales, offsets, (uint16_t*)d,
+                                              ldd, num_cus, (hipStream_t)stream));
+  }
+  if (layout == FGG_LAYOUT_MASKED) {
+    const bool fp4 = same_q(bq, FGG_E2M1X2, FGG_E8M0, 1, 32);
+    if (!fp4 && !same_q(bq, FGG_E4M3, FGG_F32, 128, 128)) return FGG_ERR_UNSUPPORTED;
+    if (M > 16) return FGG_ERR_UNSUPPORTED;
+    if (!masked_m) return FGG_ERR_INVALID_VALUE;
+    fgg_status st = device_check(&num_cus);
+    if (st != FGG_OK) return st;
+    if (M == 0 || N == 0) return FGG_OK;
+    return finish(fgg::launch_gemm_masked(fp4, G, M, N, K, (const uint8_t*)a, (const float*)a_scales,
+                                          (const uint8_t*)b, b_scales, masked_m, (uint16_t*)d, ldd,
+                                          (hipStream_t)stream));
+  }
+  return FGG_ERR_INVALID_VALUE;
+}
+
+fgg_status fgg_scaled_gemm_workspace(int64_t M, int64_t N, int64_t K, fgg_qdesc aq, fgg_qdesc bq,
+                                     const fgg_epilogue* epi, size_t* bytes) {
+  (void)N;
+  (void)K;
+  if (!bytes || M < 0) return FGG_ERR_INVALID_VALUE;
+  *bytes = 0;
+  if (same_q(aq, FGG_E2M1X2, FGG_F32, 1, 16) && same_q(bq, FGG_E2M1X2, FGG_F32, 1, 16) && epi && epi->rank > 0)
+    *bytes = fgg::w4a4_workspace_bytes(M, epi->rank);
+  return FGG_OK;
+}
+
+fgg_status fgg_scaled_gemm(int64_t M, int64_t N, int64_t K, const void* a, const void* a_scales, fgg_qdesc aq,
+                           const void* b, const void* b_scales, fgg_qdesc bq, const fgg_epilogue* epi, void* d,
+                           int64_t ldd, void* workspace, size_t ws_bytes, void* stream) {
+  if (M < 0 || N < 0 || K < 0) return FGG_ERR_INVALID_VALUE;
+  if (N % 128 != 0 || K % 128 != 0) return FGG_ERR_UNSUPPORTED;
+  if (ldd < N || ldd % 8 != 0) return FGG_ERR_INVALID_VALUE;
+  if (!a || !a_scales || !b || !b_scales || !d) return FGG_ERR_INVALID_VALUE;
+  if (!aligned(a, 16) || !aligned(b, 16) || !aligned(d, 16) || !aligned(a_scales, 4) || !aligned(b_scales, 4))
+    return FGG_ERR_INVALID_VALUE;
+  int num_cus = 0;
+  if (same_q(aq, FGG_E4M3, FGG_F32, 1, 128) && same_q(bq, FGG_E4M3, FGG_F32, 128, 128)) {
+    if (epi) return FGG_ERR_UNSUPPORTED;
+    fgg_status st = device_check(&num_cus);
+    if (st != FGG_OK) return st;
+    if (M == 0 || N == 0) return FGG_OK;
+    return finish(fgg::launch_gemm_fp8_contig(1, M, N, K, (const uint8_t*)a, (const float*)a_scales,
+                                              (const uint8_t*)b, (const float*)b_scales, nullptr, (uint16_t*)d,
+                                              ldd, num_cus, (hipStream_t)stream));
+  }
+  if (same_q(aq, FGG_E2M1X2, FGG_F32, 1, 16) && same_q(bq, FGG_E2M1X2, FGG_F32, 1, 16)) {
+    if (M % 128 != 0) return FGG_ERR_UNSUPPORTED;
+    if (!aligned(a_scales, 8) || !aligned(b_scales, 8)) return FGG_ERR_INVALID_VALUE;
+    const int32_t rank = epi ? epi->rank : 0;
+    if (rank != 0 && rank != 32) return FGG_ERR_UNSUPPORTED;
+    if (rank == 32) {
+      if (!epi->x_bf16 || !epi->l_down || !epi->l_up) return FGG_ERR_INVALID_VALUE;
+      if (!aligned(epi->x_bf16, 16) || !aligned(epi->l_down, 2) || !aligned(epi->l_up, 2))
+        return FGG_ERR_INVALID_VALUE;
+      if (!workspace || ws_bytes < fgg::w4a4_workspace_bytes(M, rank) || !aligned(workspace, 16))
+        return FGG_ERR_INVALID_VALUE;
+    }
+    const void* bias = epi ? epi->bias : nullptr;
+    if (bias && !aligned(bias, 2)) return FGG_ERR_INVALID_VALUE;
+    fgg_status st = device_check(&num_cus);
+    if (st != FGG_OK) return st;
+    if (M == 0 || N == 0) return FGG_OK;
+    return finish(fgg::launch_w4a4(M, N, K, (const uint8_t*)a, (const float*)a_scales, (const uint8_t*)b,
+                                   (const float*)b_scales, rank ? (const uint16_t*)epi->x_bf16 : nullptr,
+                                   rank ? (const uint16_t*)epi->l_down : nullptr,
+                                   rank ? (const uint16_t*)epi->l_up : nullptr, rank, (const uint16_t*)bias,
+                                   (uint16_t*)d, ldd, workspace, (hipStream_t)stream));
+  }
+  return FGG_ERR_UNSUPPORTED;
+}
+
+fgg_status fgg_moe_combine(const void* y, int64_t ldy, const int32_t* src_to_row, const float* topk_w, int64_t T,
+                           int32_t k, int64_t N, void* out, int64_t ldo, void* stream) {
+  if (T < 0 || k < 1 || k > 64 || N < 0) return FGG_ERR_INVALID_VALUE;
+  if (N % 8 != 0) return FGG_ERR_UNSUPPORTED;
+  if (ldy < N || ldo < N || ldy % 8 != 0 || ldo % 8 != 0) return FGG_ERR_INVALID_VALUE;
+  if (T == 0 || N == 0) return FGG_OK;
+  if (!y || !src_to_row || !topk_w || !out) return FGG_ERR_INVALID_VALUE;
+  if (!aligned(y, 16) || !aligned(out, 16) || !aligned(topk_w, 4)) return FGG_ERR_INVALID_VALUE;
+  fgg_status st = device_check(nullptr);
+  if (st != FGG_OK) return st;
+  return finish(fgg::launch_combine((const uint16_t*)y, ldy, src_to_row, topk_w, T, k, N, (uint16_t*)out, ldo,
+                                    (hipStream_t)stream));
+}
+
+}  // extern "C"

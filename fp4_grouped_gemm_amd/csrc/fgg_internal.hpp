@@ -1,0 +1,46 @@
+// Internal launch interface between the C-ABI layer (api.cpp) and the kernels.
+// Callers have validated every argument; these functions only enqueue work.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace fgg {
+
+enum class QuantKind { E4M3_1x128, E4M3_128x128, E2M1_1x16, E2M1_E8M0_1x32 };
+
+hipError_t launch_quantize(const void* x, bool bf16, int64_t rows, int64_t cols, int64_t ldx,
+                           QuantKind kind, bool silu, void* q, void* scales, hipStream_t st);
+
+// Permute workspace layout (bytes): hist[nblk][E] int32, base[nblk][E] int32.
+size_t permute_workspace_bytes(int64_t T, int32_t k, int32_t E);
+hipError_t launch_permute(const int32_t* ids, int64_t T, int32_t k, int32_t E, int32_t align,
+                          const uint8_t* xq, const float* xs, int64_t K, int32_t* offsets,
+                          int32_t* counts, int32_t* src_to_row, int32_t* row_to_src, uint8_t* a_out,
+                          float* sa_out, int64_t M_cap, void* ws, hipStream_t st);
+
+hipError_t launch_combine(const uint16_t* y, int64_t ldy, const int32_t* src_to_row, const float* w,
+                          int64_t T, int32_t k, int64_t N, uint16_t* out, int64_t ldo,
+                          hipStream_t st);
+
+// FP8 x FP8 grouped GEMM, contiguous layout (dense = one group with offsets {0, M}).
+// If offsets == nullptr the single group covers rows [0, M).
+hipError_t launch_gemm_fp8_contig(int32_t G, int64_t M, int64_t N, int64_t K, const uint8_t* a,
+                                  const float* sa, const uint8_t* b, const float* sb,
+                                  const int32_t* offsets, uint16_t* d, int64_t ldd, int num_cus,
+                                  hipStream_t st);
+
+// Masked (decode) layout, A e4m3 1x128; B either E2M1x2 + E8M0/32 or e4m3 128x128.
+hipError_t launch_gemm_masked(bool b_fp4, int32_t G, int64_t M, int64_t N, int64_t K,
+                              const uint8_t* a, const float* sa, const uint8_t* b, const void* sb,
+                              const int32_t* masked_m, uint16_t* d, int64_t ldd, hipStream_t st);
+
+// W4A4: E2M1 x E2M1 with fp32 per-16 scales, optional rank-r low-rank branch and bias.
+size_t w4a4_workspace_bytes(int64_t M, int32_t rank);
+hipError_t launch_w4a4(int64_t M, int64_t N, int64_t K, const uint8_t* a, const float* sa,
+                       const uint8_t* b, const float* sb, const uint16_t* x_bf16,
+                       const uint16_t* l_down, const uint16_t* l_up, int32_t rank,
+                       const uint16_t* bias, uint16_t* d, int64_t ldd, void* ws, hipStream_t st);
+
+}  // namespace fgg

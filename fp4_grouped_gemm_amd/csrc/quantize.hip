@@ -1,0 +1,225 @@
+// Block quantization kernels: fp32/bf16 -> e4m3 or E2M1 plus block scales.
+//
+// Rule ([Infra] "腾讯 AI Infra", Q "量化矩阵乘的维度和流程", per-group
+// quantization; [DeepGEMM] bhfrc.com/news/60438 §5.2, scale = max|x| / 448):
+// one scale per block from the block's largest magnitude, codes = round(x / s).
+// All kernels are HBM-bound streaming passes: each thread owns a contiguous
+// run of elements, loads it with 16-byte accesses, reduces the block maximum
+// with lane shuffles (or LDS for 128x128 blocks) and writes packed codes.
+#include "fgg_device.hpp"
+#include "fgg_internal.hpp"
+
+namespace fgg {
+
+template <bool BF16>
+__device__ inline void load8(const void* base, int64_t idx, float* f) {
+  if (BF16) {
+    const uint4 u = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(base) + idx);
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = bf16_to_f32((uint16_t)(w[i] & 0xFFFFu));
+      f[2 * i + 1] = bf16_to_f32((uint16_t)(w[i] >> 16));
+    }
+  } else {
+    const float4* p = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(base) + idx);
+    const float4 a = p[0], b = p[1];
+    f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
+    f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 1 x 128 activation groups -> e4m3, scales [cols/128][rows].
+// 16 threads per group (8 elements each); a 256-thread block covers 16 groups.
+// SILU: the row holds [gate | up] (2*cols values); a = g / (1 + e^-g) * u.
+template <bool BF16, bool SILU>
+__global__ void __launch_bounds__(256) quant_e4m3_1x128_kernel(const void* __restrict__ x, int64_t rows,
+                                                                int64_t cols, int64_t ldx,
+                                                                uint8_t* __restrict__ q,
+                                                                float* __restrict__ scales) {
+  const int64_t nkb = cols / 128;
+  const int64_t group = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int sub = threadIdx.x & 15;
+  const bool live = group < rows * nkb;
+  const int64_t row = live ? group / nkb : 0;
+  const int64_t kb = live ? group % nkb : 0;
+  const int64_t col = kb * 128 + sub * 8;
+  float v[8];
+  if (live) {
+    load8<BF16>(x, row * ldx + col, v);
+    if (SILU) {
+      float u[8];
+      load8<BF16>(x, row * ldx + cols + col, u);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = v[i] / (1.0f + expf(-v[i])) * u[i];
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = 0.0f;
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  amax = group_max<16>(amax);
+  const float s = (amax == 0.0f) ? 1.0f : amax / 448.0f;
+  if (!live) return;
+  uint32_t lo = 0, hi = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) lo |= (uint32_t)e4m3_encode(v[i] / s) << (8 * i);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) hi |= (uint32_t)e4m3_encode(v[4 + i] / s) << (8 * i);
+  *reinterpret_cast<uint2*>(q + row * cols + col) = make_uint2(lo, hi);
+  if (sub == 0) scales[kb * rows + row] = s;
+}
+
+// ---------------------------------------------------------------------------
+// 128 x 128 weight blocks -> e4m3, scales [rows/128][cols/128].
+// One 256-thread block per 128x128 block; thread t owns row t/2, 64 columns.
+template <bool BF16>
+__global__ void __launch_bounds__(256) quant_e4m3_128x128_kernel(const void* __restrict__ x, int64_t rows,
+                                                                  int64_t cols, int64_t ldx,
+                                                                  uint8_t* __restrict__ q,
+                                                                  float* __restrict__ scales) {
+  __shared__ float red[4];
+  const int64_t nkb = cols / 128;
+  const int64_t rb = blockIdx.x / nkb, kb = blockIdx.x % nkb;
+  const int64_t row = rb * 128 + (threadIdx.x >> 1);
+  const int64_t col = kb * 128 + (threadIdx.x & 1) * 64;
+  float v[64];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) load8<BF16>(x, row * ldx + col + 8 * c, v + 8 * c);
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 64; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  amax = group_max<64>(amax);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float s = (amax == 0.0f) ? 1.0f : amax / 448.0f;
+  uint8_t* dst = q + row * cols + col;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    uint32_t w[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      uint32_t word = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) word |= (uint32_t)e4m3_encode(v[16 * c + 4 * j + i] / s) << (8 * i);
+      w[j] = word;
+    }
+    *reinterpret_cast<uint4*>(dst + 16 * c) = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+  if (threadIdx.x == 0) scales[rb * nkb + kb] = s;
+}
+
+// ---------------------------------------------------------------------------
+// 1 x 16 groups -> packed E2M1 (8 bytes per group), fp32 scale = amax / 6,
+// scales [rows][cols/16].  One thread per group.
+template <bool BF16>
+__global__ void __launch_bounds__(256) quant_e2m1_1x16_kernel(const void* __restrict__ x, int64_t rows,
+                                                               int64_t cols, int64_t ldx,
+                                                               uint8_t* __restrict__ q,
+                                                               float* __restrict__ scales) {
+  const int64_t ng = cols / 16;
+  const int64_t group = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (group >= rows * ng) return;
+  const int64_t row = group / ng, g = group % ng;
+  float v[16];
+  load8<BF16>(x, row * ldx + g * 16, v);
+  load8<BF16>(x, row * ldx + g * 16 + 8, v + 8);
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  const float s = (amax == 0.0f) ? 1.0f : amax / 6.0f;
+  uint32_t w[2] = {0, 0};
+#pragma unroll
+  for (int i = 0; i < 16; ++i) w[i >> 3] |= e2m1_encode(v[i] / s) << (4 * (i & 7));
+  *reinterpret_cast<uint2*>(q + row * (cols / 2) + g * 8) = make_uint2(w[0], w[1]);
+  scales[row * ng + g] = s;
+}
+
+// ---------------------------------------------------------------------------
+// 1 x 32 groups -> packed E2M1 (16 bytes per group) with an E8M0 scale byte,
+// scales [rows][cols/32].  e = smallest integer with 6 * 2^e >= amax, read off
+// amax's fp32 bits: amax = 1.m * 2^E gives e = E - 2 when 1.m <= 1.5, else E - 1.
+__device__ inline int e8m0_exponent_of(float amax) {
+  uint32_t b = __float_as_uint(amax);
+  if (amax == 0.0f) return 0;
+  int E;
+  uint32_t mant;
+  if ((b >> 23) == 0) {                        // subnormal amax: normalize
+    const int lz = __clz(b) - 8;               // leading zeros within the 23-bit field + 1
+    E = -126 - lz;
+    mant = (b << lz) & 0x7FFFFFu;
+  } else {
+    E = (int)(b >> 23) - 127;
+    mant = b & 0x7FFFFFu;
+  }
+  int e = (mant <= 0x400000u) ? E - 2 : E - 1;
+  return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+
+template <bool BF16>
+__global__ void __launch_bounds__(256) quant_e2m1_e8m0_1x32_kernel(const void* __restrict__ x, int64_t rows,
+                                                                    int64_t cols, int64_t ldx,
+                                                                    uint8_t* __restrict__ q,
+                                                                    uint8_t* __restrict__ scales) {
+  const int64_t ng = cols / 32;
+  const int64_t group = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (group >= rows * ng) return;
+  const int64_t row = group / ng, g = group % ng;
+  float v[32];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) load8<BF16>(x, row * ldx + g * 32 + 8 * c, v + 8 * c);
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  const int e = e8m0_exponent_of(amax);
+  uint32_t w[4] = {0, 0, 0, 0};
+#pragma unroll
+  for (int i = 0; i < 32; ++i) w[i >> 3] |= e2m1_encode(ldexpf(v[i], -e)) << (4 * (i & 7));
+  *reinterpret_cast<uint4*>(q + row * (cols / 2) + g * 16) = make_uint4(w[0], w[1], w[2], w[3]);
+  scales[row * ng + g] = (uint8_t)(e + 127);
+}
+
+// ---------------------------------------------------------------------------
+hipError_t launch_quantize(const void* x, bool bf16, int64_t rows, int64_t cols, int64_t ldx,
+                           QuantKind kind, bool silu, void* q, void* scales, hipStream_t st) {
+  if (rows == 0 || cols == 0) return hipSuccess;
+  switch (kind) {
+    case QuantKind::E4M3_1x128: {
+      const int64_t groups = rows * (cols / 128);
+      dim3 grid((unsigned)((groups + 15) / 16));
+      if (bf16) {
+        if (silu) hipLaunchKernelGGL((quant_e4m3_1x128_kernel<true, true>), grid, dim3(256), 0, st, x, rows, cols, ldx, (uint8_t*)q, (float*)scales);
+        else hipLaunchKernelGGL((quant_e4m3_1x128_kernel<true, false>), grid, dim3(256), 0, st, x, rows, cols, ldx, (uint8_t*)q, (float*)scales);
+      } else {
+        if (silu) hipLaunchKernelGGL((quant_e4m3_1x128_kernel<false, true>), grid, dim3(256), 0, st, x, rows, cols, ldx, (uint8_t*)q, (float*)scales);
+        else hipLaunchKernelGGL((quant_e4m3_1x128_kernel<false, false>), grid, dim3(256), 0, st, x, rows, cols, ldx, (uint8_t*)q, (float*)scales);
+      }
+      break;
+    }
+    case QuantKind::E4M3_128x128: {
+      dim3 grid((unsigned)((rows / 128) * (cols / 128)));
+      if (bf16) hipLaunchKernelGGL((quant_e4m3_128x128_kernel<true>), grid, dim3(256), 0, st, x, rows, cols, ldx, (uint8_t*)q, (float*)scales);
+      else hipLaunchKernelGGL((quant_e4m3_128x128_kernel<false>), grid, dim3(256), 0, st, x, rows, cols, ldx, (uint8_t*)q, (float*)scales);
+      break;
+    }
+    case QuantKind::E2M1_1x16: {
+      dim3 grid((unsigned)((rows * (cols / 16) + 255) / 256));
+      if (bf16) hipLaunchKernelGGL((quant_e2m1_1x16_kernel<true>), grid, dim3(256), 0, st, x, rows, cols, ldx, (uint8_t*)q, (float*)scales);
+      else hipLaunchKernelGGL((quant_e2m1_1x16_kernel<false>), grid, dim3(256), 0, st, x, rows, cols, ldx, (uint8_t*)q, (float*)scales);
+      break;
+    }
+    case QuantKind::E2M1_E8M0_1x32: {
+      dim3 grid((unsigned)((rows * (cols / 32) + 255) / 256));
+      if (bf16) hipLaunchKernelGGL((quant_e2m1_e8m0_1x32_kernel<true>), grid, dim3(256), 0, st, x, rows, cols, ldx, (uint8_t*)q, (uint8_t*)scales);
+      else hipLaunchKernelGGL((quant_e2m1_e8m0_1x32_kernel<false>), grid, dim3(256), 0, st, x, rows, cols, ldx, (uint8_t*)q, (uint8_t*)scales);
+      break;
+    }
+  }
+  return hipGetLastError();
+}
+
+}  // namespace fgg

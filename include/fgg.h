@@ -1,0 +1,230 @@
+/*
+ * fgg.h — block-scaled FP8/FP4 MoE grouped GEMM for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of libfgg.so.  Every pointer argument is a DEVICE pointer owned by the
+ * caller unless stated otherwise; the library allocates nothing.  Every call
+ * validates its arguments on the host, enqueues its kernels on `stream` (a
+ * hipStream_t; NULL = the null stream) and returns without synchronizing.
+ * Validation failures return a status without launching anything.
+ *
+ * Sources (web pages), cited by tag and section:
+ *  [FP4MoE]   "Blackwell架构下FP4 MoE模型的TFLOPS性能优化" (intelliparadigm.com)
+ *  [W4A4]     "最新GPU架构上W4A4算子的Warp专用化内核实践" (service.ruibaoantu.com)
+ *  [Infra]    "腾讯 AI Infra" interview notes (ningzhengsheng.cn)
+ *  [MegaMoE]  Hopper + DeepGEMM MoE article (www.mqxn.cn/news/59821)
+ *  [DeepGEMM] DeepGEMM FP8 GEMM teardown (bhfrc.com/news/60438)
+ *
+ * Formats.  E4M3 is OCP FP8 e4m3 "FN" (max 448, 0x7F/0xFF NaN) — [DeepGEMM]
+ * §2.1.  E2M1 is FP4 (magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6) — [Infra] Q
+ * "FP4量化是什么"; FGG_E2M1X2 packs two per byte, element 2i in the low nibble.
+ * E8M0 is a power of two 2^(b-127).
+ *
+ * Scale layouts (fixed per quantization kind; chosen so that the GEMM kernels
+ * read one contiguous run of scales per K block):
+ *   E4M3, F32 scale, 1 × 128   (activations):  scales[K/128][rows]   (K-block-major)
+ *   E4M3, F32 scale, 128 × 128 (weights):      scales[rows/128][K/128]
+ *   E2M1X2, F32 scale, 1 × 16:                 scales[rows][K/16]
+ *   E2M1X2, E8M0 scale, 1 × 32:                scales[rows][K/32] (uint8)
+ * Code arrays are dense row-major: [rows][K] bytes (E4M3) or [rows][K/2] (E2M1X2).
+ *
+ * Thread safety: calls are stateless apart from fgg_set_num_cus(); calls on
+ * different streams may run concurrently.  Errors from the HIP runtime are
+ * reported as FGG_ERR_HIP; fgg_last_hip_error() then gives the hipError_t
+ * (per host thread).
+ */
+#ifndef FGG_H_
+#define FGG_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FGG_OK = 0,
+  FGG_ERR_INVALID_VALUE = 1, /* null required pointer, negative size, misaligned pointer, bad ld */
+  FGG_ERR_UNSUPPORTED = 2,   /* valid but not implemented: shape not a multiple of the block, dtype combo, non-gfx950 device */
+  FGG_ERR_HIP = 3            /* a HIP runtime call or kernel launch failed */
+} fgg_status;
+
+typedef enum {
+  FGG_F32 = 0,
+  FGG_BF16 = 1,
+  FGG_E4M3 = 2,
+  FGG_E2M1X2 = 3,
+  FGG_E8M0 = 4
+} fgg_dtype;
+
+/* Quantization descriptor: code type, scale type and the block one scale covers. */
+typedef struct {
+  fgg_dtype data;     /* FGG_E4M3 or FGG_E2M1X2 */
+  fgg_dtype scale;    /* FGG_F32 or FGG_E8M0 */
+  int32_t block_rows; /* 1 or 128 */
+  int32_t block_k;    /* 16, 32 or 128 */
+} fgg_qdesc;
+
+typedef enum { FGG_ACT_NONE = 0, FGG_ACT_SILU_MUL = 1 } fgg_act;
+typedef enum { FGG_LAYOUT_CONTIGUOUS = 0, FGG_LAYOUT_MASKED = 1 } fgg_layout;
+
+/* W4A4 epilogue ([W4A4] §1: Y = (Q(X)·Q(W)ᵀ) ⊙ scale + L(X) + b).  All fields may be NULL/0. */
+typedef struct {
+  const void* x_bf16; /* [M][K] bf16, row-major: the unquantized input read by the low-rank branch */
+  const void* l_down; /* [K][rank] bf16, row-major */
+  const void* l_up;   /* [rank][N] bf16, row-major */
+  int32_t rank;       /* 0 (no low-rank branch) or 32 */
+  const void* bias;   /* [N] bf16, the per-column affine term */
+} fgg_epilogue;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* fgg_status_string(fgg_status s);
+
+/* hipError_t behind the last FGG_ERR_HIP returned on this host thread (0 if none). */
+int fgg_last_hip_error(void);
+
+/* Number of workgroup slots per "wave" of the persistent GEMM grids: the
+ * compute-unit count the persistent kernels size their grid for
+ * ([MegaMoE] §4.1 exposes the same knob as an SM count).  0 restores the
+ * device's CU count.  Negative values: FGG_ERR_INVALID_VALUE. */
+fgg_status fgg_set_num_cus(int n);
+
+/*
+ * fgg_quantize_blockwise — online/offline block quantization.
+ *
+ * [Infra] Q "量化矩阵乘的维度和流程": every block shares one scale and the code
+ * is round(x / scale); [DeepGEMM] §5.2: scale = max|x| / 448 for e4m3 (6 for
+ * E2M1, its largest magnitude).  For each block:
+ *   E4M3 / F32:  s = fl32(amax / 448); code = e4m3_rne_satfinite(fl32(x / s))
+ *   E2M1 / F32:  s = fl32(amax / 6);   code = e2m1_rne_satfinite(fl32(x / s))
+ *   E2M1 / E8M0: e = smallest integer with 6·2^e >= amax (clamped to
+ *                [-127,127]); code = e2m1_rne(x · 2^-e); scale byte = e + 127
+ * An all-zero block gets scale 1 (E8M0 byte 127).  Ties round to the even
+ * code; magnitudes beyond the format's max saturate; signs (also of zero) are
+ * kept.  Divisions are IEEE fp32.
+ *
+ * x:       [rows][ldx] elements of x_dtype (FGG_F32 or FGG_BF16); only the first
+ *          `cols` (or 2·cols for FGG_ACT_SILU_MUL) of each row are read.
+ * act:     FGG_ACT_SILU_MUL quantizes a = g / (1 + e^-g) · u computed in fp32,
+ *          where row r holds [g | u] = x[r][0:cols], x[r][cols:2·cols]
+ *          (SiLU of [MegaMoE] §3.1 on the gate half of a gate-up output);
+ *          only with q = {E4M3, F32, 1, 128}.
+ * q:       one of {E4M3,F32,1,128}, {E4M3,F32,128,128}, {E2M1X2,F32,1,16},
+ *          {E2M1X2,E8M0,1,32}.
+ * q_out:   codes, dense [rows][cols] (E4M3) or [rows][cols/2] (E2M1X2).
+ * scales_out: in the layout of the quantization kind (see top of file).
+ * Requires cols % block_k == 0 and, for 128-row blocks, rows % 128 == 0
+ * (else FGG_ERR_UNSUPPORTED).  rows == 0 is a no-op.
+ */
+fgg_status fgg_quantize_blockwise(const void* x, fgg_dtype x_dtype, int64_t rows, int64_t cols,
+                                  int64_t ldx, fgg_act act, fgg_qdesc q, void* q_out,
+                                  void* scales_out, void* stream);
+
+/*
+ * fgg_moe_permute — expert histogram, padded prefix sum and stable scatter.
+ *
+ * [DeepGEMM] §5.3 (pass group ids and token offsets; keep each expert's rows
+ * contiguous) and [FP4MoE] §4.2 (expert group sizes a multiple of 128).
+ * Pair p = t·k + j routes token t to expert topk_ids[p].  Ids outside [0, E)
+ * are dropped (not routed on this GPU).  Then
+ *   counts[e]   = number of pairs routed to e
+ *   offsets[e]  = Σ_{e' < e} ceil(counts[e'] / align) · align,  offsets[E] = M_total
+ *   src_to_row[p] = offsets[e] + (number of pairs p' < p routed to e), or -1 if dropped
+ *   row_to_src[r] = p for routed rows, -1 for padding rows and rows >= M_total
+ * and, when xq is non-NULL, the permuted activations:
+ *   a_out[r][:]   = xq[p / k][:]  (e4m3 codes, K bytes per row), 0 for padding rows
+ *   sa_out[kb][r] = xs[kb][p / k] (1×128 scales, K-block-major), 0 for padding rows
+ * Rows in [M_total, M_cap) of a_out/sa_out are not written.  If M_total > M_cap
+ * (M_cap too small) no row at or beyond M_cap is written and offsets[E] still
+ * reports M_total, so the caller can detect it.  M_cap = T·k + E·(align-1) is
+ * always enough.
+ *
+ * topk_ids: [T][k] int32.  xq: [T][K] e4m3 codes or NULL (index-only mode).
+ * xs: [K/128][T] fp32 (ignored when xq is NULL).  K % 128 == 0.
+ * offsets [E+1], counts [E], src_to_row [T·k], row_to_src [M_cap] int32.
+ * a_out [M_cap][K] bytes, sa_out [K/128][M_cap] fp32.
+ * workspace: device scratch of at least fgg_moe_permute_workspace() bytes.
+ * Limits: 1 <= E <= 1024, 1 <= k <= 64, align in {1..1024} (128 for the
+ * GEMMs).  T == 0 writes offsets = 0 and nothing else.
+ */
+fgg_status fgg_moe_permute_workspace(int64_t T, int32_t k, int32_t E, size_t* bytes);
+fgg_status fgg_moe_permute(const int32_t* topk_ids, int64_t T, int32_t k, int32_t E, int32_t align,
+                           const void* xq, const float* xs, int64_t K, int32_t* offsets,
+                           int32_t* counts, int32_t* src_to_row, int32_t* row_to_src, void* a_out,
+                           float* sa_out, int64_t M_cap, void* workspace, size_t ws_bytes,
+                           void* stream);
+
+/*
+ * fgg_grouped_gemm_scaled — one launch for all groups (experts).
+ *
+ * The per-group formula of [Infra] Q "量化矩阵乘的维度和流程" with both
+ * operands' scales applied to each K block inside the K loop and FP32
+ * accumulation over all of K ([DeepGEMM] §2.2, §2.3):
+ *   D[r][n] = bf16_rne( Σ_kb sA[r,kb] · sB[g,n,kb] · Σ_{k in kb} A[r][k] · B[g][n][k] )
+ * with B stored [G][N][K] (the Q(W)ᵀ orientation of [W4A4] §1).
+ *
+ * FGG_LAYOUT_CONTIGUOUS (prefill): rows [offsets[g], offsets[g+1]) of A use
+ *   expert g; M is the row count of A, sA and D (e.g. M_cap of the permute);
+ *   every offsets[g] must be a multiple of 128 (moe_permute with align 128
+ *   guarantees it) and offsets[G] <= M.  Rows >= offsets[G] are not read
+ *   or written.  aq = {E4M3,F32,1,128}: a [M][K], a_scales [K/128][M];
+ *   bq = {E4M3,F32,128,128}: b [G][N][K], b_scales [G][N/128][K/128].
+ * FGG_LAYOUT_MASKED (decode): A is [G][M][K] (M = rows per group, <= 16);
+ *   group g uses rows m < masked_m[g] (values clamped to [0, M]); other rows
+ *   are neither read nor written.  aq = {E4M3,F32,1,128}: a_scales
+ *   [G][K/128][M].  bq = {E2M1X2,E8M0,1,32}: b [G][N][K/2],
+ *   b_scales [G][N][K/32] uint8 (the E8M0 scale multiplies each 32-element
+ *   block inside the MFMA); or bq = {E4M3,F32,128,128} as above.
+ *   D is [G][M][ldd].
+ * d: bf16, row stride ldd >= N.  N % 128 == 0, K % 128 == 0, 1 <= G <= 1024.
+ * Device-side values of offsets / masked_m are trusted within these rules.
+ */
+fgg_status fgg_grouped_gemm_scaled(fgg_layout layout, int32_t G, int64_t M, int64_t N, int64_t K,
+                                   const void* a, const void* a_scales, fgg_qdesc aq,
+                                   const void* b, const void* b_scales, fgg_qdesc bq,
+                                   const int32_t* offsets, const int32_t* masked_m, void* d,
+                                   int64_t ldd, void* stream);
+
+/*
+ * fgg_scaled_gemm — the dense one-group case ([MegaMoE] §2.1 fp8_gemm with
+ * fine-grained scales), and the W4A4 operator of [W4A4] §1.
+ *
+ * aq = {E4M3,F32,1,128}, bq = {E4M3,F32,128,128}: identical (bit for bit) to
+ *   fgg_grouped_gemm_scaled(CONTIGUOUS, G = 1, offsets = {0, M}); any M >= 0
+ *   (a partial last row block is handled).  epi must be NULL.
+ * aq = bq = {E2M1X2,F32,1,16} (W4A4): a [M][K/2], a_scales [M][K/16];
+ *   b [N][K/2], b_scales [N][K/16];
+ *   D = bf16( Σ_g16 sA[m,g]·sB[n,g]·Σ_{k in g} A[m][k]·B[n][k]
+ *             + (x_bf16 · l_down) · l_up + bias )
+ *   The operands are dequantized on chip to fp16 (x·s rounded once) and
+ *   contracted with fp16 MFMA in fp32; the rank-`rank` intermediate is
+ *   rounded to fp16.  Requires M % 128 == 0, K % 128 == 0, N % 128 == 0.
+ *   With a low-rank branch, workspace must hold fgg_scaled_gemm_workspace()
+ *   bytes (the [M][rank] intermediate).
+ */
+fgg_status fgg_scaled_gemm_workspace(int64_t M, int64_t N, int64_t K, fgg_qdesc aq, fgg_qdesc bq,
+                                     const fgg_epilogue* epi, size_t* bytes);
+fgg_status fgg_scaled_gemm(int64_t M, int64_t N, int64_t K, const void* a, const void* a_scales,
+                           fgg_qdesc aq, const void* b, const void* b_scales, fgg_qdesc bq,
+                           const fgg_epilogue* epi, void* d, int64_t ldd, void* workspace,
+                           size_t ws_bytes, void* stream);
+
+/*
+ * fgg_moe_combine — gate-weighted un-permute ([MegaMoE] §1 and §3: the
+ * selected experts' outputs are summed with the gate weights).
+ *   out[t][n] = bf16_rne( Σ_{j = 0..k-1, src_to_row[t·k+j] >= 0} w[t][j] · y[src_to_row[t·k+j]][n] )
+ * summed in fp32 in increasing j (deterministic); a token with no routed slot
+ * gets +0.
+ * y: bf16 [rows][ldy]; src_to_row: [T·k] int32 (from moe_permute);
+ * topk_w: [T][k] fp32; out: bf16 [T][ldo].  N % 8 == 0, ldy/ldo >= N and
+ * multiples of 8.
+ */
+fgg_status fgg_moe_combine(const void* y, int64_t ldy, const int32_t* src_to_row,
+                           const float* topk_w, int64_t T, int32_t k, int64_t N, void* out,
+                           int64_t ldo, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FGG_H_ */

@@ -1,0 +1,107 @@
+"""CPU checks of the C ABI: libfgg.so loads, exports every function that
+include/fgg.h declares, and rejects bad arguments on the host before any
+device work (these calls return before touching HIP)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import fp4_grouped_gemm_amd as fgg
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fgg.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(fgg.library_path()),
+                                reason="libfgg.so not built (run __graft_entry__.build())")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fgg_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = _declared()
+    for n in ["fgg_quantize_blockwise", "fgg_moe_permute", "fgg_moe_permute_workspace", "fgg_grouped_gemm_scaled",
+              "fgg_scaled_gemm", "fgg_scaled_gemm_workspace", "fgg_moe_combine", "fgg_status_string",
+              "fgg_last_hip_error", "fgg_set_num_cus"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(fgg.library_path())
+    missing = [n for n in _declared() if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_status_strings_and_knobs():
+    lib = fgg.load_library()
+    assert lib.fgg_status_string(0) == b"FGG_OK"
+    assert lib.fgg_status_string(2) == b"FGG_ERR_UNSUPPORTED"
+    assert lib.fgg_set_num_cus(-1) == 1
+    assert lib.fgg_set_num_cus(0) == 0
+
+
+def _q(t):
+    return fgg.QDesc(*t)
+
+
+def test_quantize_rejects_bad_arguments_on_host():
+    lib = fgg.load_library()
+    P = ctypes.c_void_p
+    good = P(4096)
+    # negative rows
+    assert lib.fgg_quantize_blockwise(good, fgg.FGG_F32, -1, 128, 128, 0, _q(fgg.Q_E4M3_1x128), good, good, None) == 1
+    # unsupported descriptor
+    assert lib.fgg_quantize_blockwise(good, fgg.FGG_F32, 4, 128, 128, 0, _q((fgg.FGG_E4M3, fgg.FGG_F32, 1, 64)),
+                                      good, good, None) == 2
+    # cols not a multiple of the block
+    assert lib.fgg_quantize_blockwise(good, fgg.FGG_F32, 4, 100, 128, 0, _q(fgg.Q_E4M3_1x128), good, good, None) == 2
+    # 128-row blocks with a ragged row count
+    assert lib.fgg_quantize_blockwise(good, fgg.FGG_F32, 100, 128, 128, 0, _q(fgg.Q_E4M3_128x128), good, good,
+                                      None) == 2
+    # SiLU only with the 1x128 e4m3 kind
+    assert lib.fgg_quantize_blockwise(good, fgg.FGG_BF16, 4, 32, 64, 1, _q(fgg.Q_E2M1_E8M0_1x32), good, good,
+                                      None) == 2
+    # null pointers / short leading dimension / misalignment
+    assert lib.fgg_quantize_blockwise(None, fgg.FGG_F32, 4, 128, 128, 0, _q(fgg.Q_E4M3_1x128), good, good, None) == 1
+    assert lib.fgg_quantize_blockwise(good, fgg.FGG_F32, 4, 256, 128, 0, _q(fgg.Q_E4M3_1x128), good, good, None) == 1
+    assert lib.fgg_quantize_blockwise(P(4097), fgg.FGG_F32, 4, 128, 128, 0, _q(fgg.Q_E4M3_1x128), good, good,
+                                      None) == 1
+    # empty input is a successful no-op even without a device
+    assert lib.fgg_quantize_blockwise(None, fgg.FGG_F32, 0, 128, 128, 0, _q(fgg.Q_E4M3_1x128), None, None, None) == 0
+
+
+def test_gemm_and_permute_reject_bad_arguments_on_host():
+    lib = fgg.load_library()
+    P = ctypes.c_void_p
+    g = P(4096)
+    A, B8, B4 = _q(fgg.Q_E4M3_1x128), _q(fgg.Q_E4M3_128x128), _q(fgg.Q_E2M1_E8M0_1x32)
+    # N not a multiple of 128
+    assert lib.fgg_grouped_gemm_scaled(0, 2, 256, 100, 256, g, g, A, g, g, B8, g, None, g, 128, None) == 2
+    # K not a multiple of 128
+    assert lib.fgg_grouped_gemm_scaled(0, 2, 256, 128, 200, g, g, A, g, g, B8, g, None, g, 128, None) == 2
+    # contiguous layout needs offsets; masked needs masked_m and M <= 16
+    assert lib.fgg_grouped_gemm_scaled(0, 2, 256, 128, 256, g, g, A, g, g, B8, None, None, g, 128, None) == 1
+    assert lib.fgg_grouped_gemm_scaled(1, 2, 16, 128, 256, g, g, A, g, g, B4, None, None, g, 128, None) == 1
+    assert lib.fgg_grouped_gemm_scaled(1, 2, 17, 128, 256, g, g, A, g, g, B4, None, g, g, 128, None) == 2
+    # FP4 weights are not a contiguous-layout operand
+    assert lib.fgg_grouped_gemm_scaled(0, 2, 256, 128, 256, g, g, A, g, g, B4, g, None, g, 128, None) == 2
+    # ldd smaller than N, bad G
+    assert lib.fgg_grouped_gemm_scaled(0, 2, 256, 256, 256, g, g, A, g, g, B8, g, None, g, 128, None) == 1
+    assert lib.fgg_grouped_gemm_scaled(0, 0, 256, 128, 256, g, g, A, g, g, B8, g, None, g, 128, None) == 1
+    # dense W4A4 with an unsupported rank
+    epi = fgg.Epilogue(4096, 4096, 4096, 16, None)
+    W = _q(fgg.Q_E2M1_1x16)
+    assert lib.fgg_scaled_gemm(256, 128, 256, g, g, W, g, g, W, ctypes.byref(epi), g, 128, g, 1 << 20, None) == 2
+    # permute: bad k / E, missing workspace
+    assert lib.fgg_moe_permute(g, 10, 0, 4, 128, None, None, 0, g, g, g, g, None, None, 100, g, 1 << 20, None) == 1
+    assert lib.fgg_moe_permute(g, 10, 2, 2000, 128, None, None, 0, g, g, g, g, None, None, 100, g, 1 << 20, None) == 1
+    assert lib.fgg_moe_permute(g, 10, 2, 4, 128, None, None, 0, g, g, g, g, None, None, 100, None, 0, None) == 1
+    n = ctypes.c_size_t(0)
+    assert lib.fgg_moe_permute_workspace(10, 2, 4, ctypes.byref(n)) == 0 and n.value > 0
+    # combine: N not a multiple of 8
+    assert lib.fgg_moe_combine(g, 16, g, g, 4, 2, 12, g, 16, None) == 2

@@ -1,0 +1,365 @@
+"""GPU parity for the grouped / dense / masked / W4A4 GEMMs against the oracle.
+
+Tolerance (floating point): |y - y_ref| <= 1e-2 · (|y_ref| + rms(y_ref)), with
+y_ref the oracle's fp64 result rounded to bf16.  Padding rows must be exactly
+zero; one group must equal the dense call bit for bit; runs are deterministic.
+Small cases compare every output; the full-size cases compare sampled rows
+(all columns) that the oracle computes one by one."""
+
+import numpy as np
+import pytest
+import torch
+
+import fp4_grouped_gemm_amd as fgg
+import oracle
+import synth
+from oracle import formats as F
+from _util import cuda, to_np, tol_check
+
+pytestmark = pytest.mark.gpu
+
+
+def _quant_weights_gpu(w_np, qdesc):
+    """Quantize a [G, N, K] weight stack on the GPU, expert by expert."""
+    G, N, K = w_np.shape
+    outs, scales = [], []
+    for e in range(G):
+        q, s = fgg.quantize_blockwise(cuda(w_np[e]), qdesc)
+        outs.append(q)
+        scales.append(s)
+    return torch.stack(outs), torch.stack(scales)
+
+
+def _quant_weights_oracle(w_np):
+    G, N, K = w_np.shape
+    bq = np.empty((G, N, K), np.uint8)
+    sb = np.empty((G, N // 128, K // 128), np.float32)
+    for e in range(G):
+        bq[e], sb[e] = oracle.quantize_e4m3_blocks(w_np[e], 128, 128)
+    return bq, sb
+
+
+# ------------------------------------------------------------ one-hot probes
+
+def test_one_hot_probe_contiguous():
+    """A single 1.0 at (r, k) in A and at (n, k) of expert g in B lands on
+    exactly (r, n), scaled by the distinct power-of-two block scales that
+    belong to (r, k/128) and (g, n/128, k/128)."""
+    G, N, K = 3, 256, 512
+    offsets = np.array([0, 128, 128, 384], np.int32)      # expert 1 is empty
+    M = 384
+    for (r, n, k, g) in [(0, 0, 0, 0), (127, 255, 511, 0), (130, 17, 300, 2), (383, 128, 129, 2), (200, 64, 64, 2),
+                         (5, 3, 3, 2), (300, 40, 500, 0)]:
+        a = np.zeros((M, K), np.uint8)
+        a[r, k] = 0x38
+        b = np.zeros((G, N, K), np.uint8)
+        b[g, n, k] = 0x38
+        sa = np.ldexp(1.0, (np.arange(M)[None, :] % 7) + 3 * np.arange(K // 128)[:, None] - 8).astype(np.float32)
+        sb = np.ldexp(1.0, np.arange(G * (N // 128) * (K // 128)).reshape(G, N // 128, K // 128) % 11 - 5).astype(np.float32)
+        y = to_np(fgg.grouped_gemm_scaled(cuda(a), cuda(sa), cuda(b), cuda(sb), offsets=cuda(offsets)))
+        expect = np.zeros((M, N))
+        if np.searchsorted(offsets, r, side="right") - 1 == g:    # row r belongs to expert g
+            expect[r, n] = sa[k // 128, r] * sb[g, n // 128, k // 128]
+        assert np.array_equal(y, expect), (r, n, k, g)
+
+
+def test_one_hot_probe_masked_fp4():
+    """E2M1 operand layout, nibble order and per-32 E8M0 scale placement."""
+    G, M, N, K = 2, 16, 128, 256
+    masked = np.array([16, 9], np.int32)
+    for (g, m, n, k) in [(0, 0, 0, 0), (0, 15, 127, 255), (1, 8, 33, 31), (1, 3, 64, 32), (0, 5, 16, 161), (1, 0, 1, 95)]:
+        a = np.zeros((G, M, K), np.uint8)
+        a[g, m, k] = 0x38
+        b = np.zeros((G, N, K // 2), np.uint8)
+        b[g, n, k // 2] = 0x2 << (4 * (k % 2))             # 1.0 in the nibble of element k
+        sa = np.ldexp(1.0, np.arange(G * (K // 128) * M).reshape(G, K // 128, M) % 5 - 2).astype(np.float32)
+        be = (127 + (np.arange(G * N * (K // 32)).reshape(G, N, K // 32) % 9) - 4).astype(np.uint8)
+        y = to_np(fgg.grouped_gemm_scaled(cuda(a), cuda(sa), cuda(b), cuda(be), masked_m=cuda(masked),
+                                          b_qdesc=fgg.Q_E2M1_E8M0_1x32))
+        expect = np.zeros((G, M, N))
+        expect[g, m, n] = sa[g, k // 128, m] * 2.0 ** (int(be[g, n, k // 32]) - 127)
+        for gg in range(G):
+            mm = masked[gg]
+            assert np.array_equal(y[gg, :mm], expect[gg, :mm]), (g, m, n, k)
+
+
+# ------------------------------------------------------- contiguous / dense
+
+def _contig_case(seed, counts, N, K):
+    G = len(counts)
+    padded = [-(-c // 128) * 128 for c in counts]
+    offsets = np.concatenate([[0], np.cumsum(padded)]).astype(np.int32)
+    M = int(offsets[-1]) + 64                 # extra rows beyond offsets[G] are never touched
+    g = synth.rng(seed)
+    x = synth.normal(g, (M, K))
+    for e in range(G):                         # padding rows hold zeros, as after the permute
+        x[offsets[e] + counts[e]:offsets[e + 1]] = 0
+    w = synth.normal(g, (G, N, K), 0.02)
+    return x, w, offsets
+
+
+@pytest.mark.parametrize("counts,N,K", [([5, 0, 300, 128], 256, 512), ([1], 128, 128), ([129, 1000], 384, 1024)])
+def test_grouped_contiguous_small(counts, N, K):
+    x, w, offsets = _contig_case(len(counts) * 31 + N, counts, N, K)
+    xq, xs = fgg.quantize_blockwise(cuda(x), fgg.Q_E4M3_1x128)
+    bq, sb = _quant_weights_gpu(w, fgg.Q_E4M3_128x128)
+    d = torch.full((x.shape[0], N), float("nan"), dtype=torch.bfloat16, device="cuda")
+    fgg.grouped_gemm_scaled(xq, xs, bq, sb, offsets=cuda(offsets), out=d)
+    y = to_np(d)
+    aq_r, sa_r = oracle.quantize_e4m3_blocks(x, 1, 128)
+    bq_r, sb_r = _quant_weights_oracle(w)
+    assert np.array_equal(to_np(xq), aq_r) and np.array_equal(to_np(bq), bq_r)
+    mt = int(offsets[-1])
+    ref = oracle.round_bf16(oracle.grouped_gemm_contiguous(aq_r, sa_r, bq_r, sb_r, offsets))[:mt]
+    tol_check(y[:mt], ref, what="grouped contiguous")
+    for e in range(len(counts)):                               # padding rows are exactly +0
+        pad = y[offsets[e] + counts[e]:offsets[e + 1]]
+        assert np.all(pad == 0) and not np.any(np.signbit(pad))
+    assert np.all(np.isnan(y[mt:]))                            # rows >= offsets[G] untouched
+
+
+@pytest.mark.parametrize("M,N,K", [(500, 256, 1024), (128, 128, 128), (1, 128, 256)])
+def test_dense_small_and_one_group_identity(M, N, K):
+    g = synth.rng(M + N + K)
+    x = synth.normal(g, (M, K))
+    w = synth.normal(g, (N, K), 0.02)
+    xq, xs = fgg.quantize_blockwise(cuda(x), fgg.Q_E4M3_1x128)
+    bq, sb = fgg.quantize_blockwise(cuda(w), fgg.Q_E4M3_128x128)
+    y = fgg.scaled_gemm(xq, xs, bq, sb)
+    aq_r, sa_r = oracle.quantize_e4m3_blocks(x, 1, 128)
+    bq_r, sb_r = oracle.quantize_e4m3_blocks(w, 128, 128)
+    ref = oracle.round_bf16(oracle.scaled_gemm_dense(aq_r, sa_r, bq_r, sb_r))
+    tol_check(to_np(y), ref, what="dense")
+    # the grouped call with one group covering [0, M) is the same computation
+    y1 = fgg.grouped_gemm_scaled(xq, xs, bq[None], sb[None], offsets=cuda(np.array([0, M], np.int32)))
+    if M % 128 == 0:
+        assert torch.equal(y1, y)
+    else:
+        assert torch.equal(y1[:M], y[:M])
+
+
+def test_dense_full_size_sampled_and_deterministic():
+    w = synth.dense()
+    M, N, K = w["M"], w["N"], w["K"]
+    xq, xs = fgg.quantize_blockwise(cuda(w["x"]), fgg.Q_E4M3_1x128)
+    bq, sb = fgg.quantize_blockwise(cuda(w["w"]), fgg.Q_E4M3_128x128)
+    y = fgg.scaled_gemm(xq, xs, bq, sb)
+    y2 = fgg.scaled_gemm(xq, xs, bq, sb)
+    assert torch.equal(y, y2)
+    rows = np.array([0, 1, 127, 128, 2047, 2100, 4000, 4095])
+    aq_r, sa_r = oracle.quantize_e4m3_blocks(w["x"][rows], 1, 128)
+    bq_r, sb_r = oracle.quantize_e4m3_blocks(w["w"], 128, 128)
+    assert np.array_equal(to_np(xq)[rows], aq_r) and np.array_equal(to_np(bq), bq_r)
+    ref = oracle.round_bf16(oracle.scaled_gemm_dense(aq_r, sa_r, bq_r, sb_r))
+    tol_check(to_np(y)[rows], ref, what="dense 4096x4096x7168 sampled rows")
+
+
+# ------------------------------------------------------------- MoE chains
+
+def _moe_chain_gpu(x, topk_ids, topk_w, E, wq_gu, ws_gu, wq_dn=None, ws_dn=None):
+    xq, xs = fgg.quantize_blockwise(cuda(x), fgg.Q_E4M3_1x128)
+    perm = fgg.moe_permute(cuda(topk_ids), E, 128, xq=xq, xs=xs)
+    h = fgg.grouped_gemm_scaled(perm["a"], perm["sa"], wq_gu, ws_gu, offsets=perm["offsets"])
+    if wq_dn is None:
+        y = h
+    else:
+        a2, s2 = fgg.quantize_blockwise(h, fgg.Q_E4M3_1x128, silu_mul=True)
+        y = fgg.grouped_gemm_scaled(a2, s2, wq_dn, ws_dn, offsets=perm["offsets"])
+    out = fgg.moe_combine(y, perm["src_to_row"], cuda(topk_w))
+    return out, perm, h, y
+
+
+def test_tiny_moe_end_to_end():
+    w = synth.tiny_moe()
+    T, E, k = w["T"], w["E"], w["k"]
+    bq, sb = _quant_weights_gpu(w["w"], fgg.Q_E4M3_128x128)
+    out, perm, h, _ = _moe_chain_gpu(w["x"], w["topk_ids"], w["topk_w"], E, bq, sb)
+    # oracle chain
+    aq_r, sa_r = oracle.quantize_e4m3_blocks(w["x"], 1, 128)
+    p = oracle.moe_permute(w["topk_ids"], E, 128)
+    mt = int(p["offsets"][-1])
+    a_r, s_r = oracle.gather_permuted(p["row_to_src"], mt, k, aq_r, sa_r)
+    bq_r, sb_r = _quant_weights_oracle(w["w"])
+    h_r = oracle.round_bf16(oracle.grouped_gemm_contiguous(a_r, s_r, bq_r, sb_r, p["offsets"]))
+    tol_check(to_np(h)[:mt], h_r, what="tiny MoE expert outputs")
+    out_r = oracle.round_bf16(oracle.moe_combine(h_r, p["src_to_row"], w["topk_w"], T, k))
+    tol_check(to_np(out), out_r, what="tiny MoE combined output")
+    assert out.shape == (64, 512)
+
+
+def test_moe_prefill_full_size_sampled():
+    cfg = synth.MOE_PREFILL
+    T, K, E, k = cfg["T"], cfg["K"], cfg["E"], cfg["k"]
+    Ngu, Ndn, Kdn = cfg["N_gu"], cfg["N_dn"], cfg["K_dn"]
+    r = synth.moe_prefill_routing()
+    x = synth.moe_prefill_x()
+    gu_q, gu_s, dn_q, dn_s = [], [], [], []
+    w_keep = {}
+    sample_experts = [0, 7, 31]
+    for e in range(E):
+        wgu = synth.moe_prefill_expert_weight(1003, "gu", e, Ngu, K)
+        wdn = synth.moe_prefill_expert_weight(1003, "dn", e, Ndn, Kdn)
+        q, s = fgg.quantize_blockwise(cuda(wgu), fgg.Q_E4M3_128x128)
+        gu_q.append(q); gu_s.append(s)
+        q, s = fgg.quantize_blockwise(cuda(wdn), fgg.Q_E4M3_128x128)
+        dn_q.append(q); dn_s.append(s)
+        if e in sample_experts:
+            w_keep[e] = (wgu, wdn)
+    gu_q, gu_s = torch.stack(gu_q), torch.stack(gu_s)
+    dn_q, dn_s = torch.stack(dn_q), torch.stack(dn_s)
+    out, perm, h, y = _moe_chain_gpu(x, r["topk_ids"], r["topk_w"], E, gu_q, gu_s, dn_q, dn_s)
+    offsets = to_np(perm["offsets"]).astype(np.int64)
+    counts = to_np(perm["counts"])
+    r2s = to_np(perm["row_to_src"])
+    a_all = to_np(perm["a"])
+    sa_all = to_np(perm["sa"])
+    h_np = to_np(h)
+    for e in sample_experts:
+        rows = offsets[e] + np.unique(np.linspace(0, counts[e] - 1, 6).astype(np.int64))
+        rows = np.concatenate([rows, [offsets[e + 1] - 1]])                 # a padding row
+        wgu, wdn = w_keep[e]
+        bq_r, sb_r = oracle.quantize_e4m3_blocks(wgu, 128, 128)
+        assert np.array_equal(to_np(gu_q[e]), bq_r)
+        a_r = a_all[rows]
+        sa_r = sa_all[:, rows].T
+        # the permuted rows are the token rows quantized by the oracle
+        toks = r2s[rows] // k
+        valid = r2s[rows] >= 0
+        aq_tok, sa_tok = oracle.quantize_e4m3_blocks(x[toks[valid]], 1, 128)
+        assert np.array_equal(a_r[valid], aq_tok) and np.array_equal(sa_r[valid], sa_tok)
+        h_ref = oracle.round_bf16(oracle.grouped_gemm_contiguous(
+            a_r, sa_r, bq_r[None], sb_r[None], np.array([0, len(rows)])))
+        tol_check(h_np[rows], h_ref, what=f"prefill gate-up expert {e}")
+        assert np.all(h_np[offsets[e + 1] - 1] == 0) or counts[e] % 128 == 0
+        # down projection of the same rows from the GPU's own gate-up output
+        a2_r, s2_r = oracle.silu_mul_quantize(h_np[rows].astype(np.float64))
+        bq2, sb2 = oracle.quantize_e4m3_blocks(wdn, 128, 128)
+        y_ref = oracle.round_bf16(oracle.grouped_gemm_contiguous(
+            a2_r, s2_r, bq2[None], sb2[None], np.array([0, len(rows)])))
+        tol_check(to_np(y)[rows], y_ref, what=f"prefill down expert {e}")
+    # combine for a sample of tokens, from the GPU's own expert outputs
+    toks = np.arange(0, T, 997)
+    y_np = to_np(y)
+    s2r = to_np(perm["src_to_row"])
+    ref = oracle.round_bf16(oracle.moe_combine(y_np, s2r.reshape(T, k)[toks].reshape(-1),
+                                               r["topk_w"][toks], len(toks), k))
+    tol_check(to_np(out)[toks], ref, what="prefill combine")
+
+
+# ----------------------------------------------------------------- masked
+
+def _masked_case(G, M, N, K, seed, masked=None):
+    g = synth.rng(seed)
+    if masked is None:
+        masked = g.integers(1, M + 1, size=G).astype(np.int32)
+    x = synth.normal(g, (G, M, K))
+    w = synth.normal(g, (G, N, K), 0.02)
+    return x, w, masked
+
+
+def _quant_masked_a_gpu(x):
+    G, M, K = x.shape
+    aq, sa = fgg.quantize_blockwise(cuda(x.reshape(G * M, K)), fgg.Q_E4M3_1x128)
+    # [K/128, G*M] -> [G, K/128, M]
+    sa = sa.reshape(K // 128, G, M).permute(1, 0, 2).contiguous()
+    return aq.reshape(G, M, K), sa
+
+
+@pytest.mark.parametrize("G,M,N,K,masked", [(4, 16, 256, 512, [16, 1, 0, 7]), (3, 5, 128, 128, [5, 5, 2]),
+                                            (2, 16, 640, 1024, None)])
+def test_masked_fp4_small(G, M, N, K, masked):
+    x, w, mm = _masked_case(G, M, N, K, G * 100 + N, None if masked is None else np.array(masked, np.int32))
+    aq, sa = _quant_masked_a_gpu(x)
+    bq, be = _quant_weights_gpu(w, fgg.Q_E2M1_E8M0_1x32)
+    d = torch.full((G, M, N), float("nan"), dtype=torch.bfloat16, device="cuda")
+    fgg.grouped_gemm_scaled(aq, sa, bq, be, masked_m=cuda(mm), b_qdesc=fgg.Q_E2M1_E8M0_1x32, out=d)
+    y = to_np(d)
+    aq_r, sa_r = oracle.quantize_e4m3_blocks(x.reshape(G * M, K), 1, 128)
+    aq_r, sa_r = aq_r.reshape(G, M, K), sa_r.reshape(G, M, K // 128)
+    bc = np.empty((G, N, K), np.uint8)
+    be_r = np.empty((G, N, K // 32), np.uint8)
+    for e in range(G):
+        bc[e], be_r[e] = oracle.quantize_e2m1_e8m0_groups(w[e], 32)
+    bp_r = F.pack_e2m1x2(bc)
+    assert np.array_equal(to_np(bq), bp_r) and np.array_equal(to_np(be), be_r)
+    ref = oracle.round_bf16(oracle.grouped_gemm_masked(aq_r, sa_r, bp_r, be_r, mm))
+    for e in range(G):
+        m = int(mm[e])
+        tol_check(y[e, :m], ref[e, :m], what=f"masked fp4 group {e}")
+        assert np.all(np.isnan(y[e, m:]))                       # rows >= masked_m untouched
+
+
+def test_masked_fp4_full_size_sampled():
+    wl = synth.moe_decode(with_weights=False)
+    G, M, N, K = wl["G"], wl["M_max"], wl["N"], wl["K"]
+    mm = wl["masked_m"]
+    aq, sa = _quant_masked_a_gpu(wl["x"])
+    bq = torch.empty((G, N, K // 2), dtype=torch.uint8, device="cuda")
+    be = torch.empty((G, N, K // 32), dtype=torch.uint8, device="cuda")
+    keep = {}
+    for e in range(G):
+        we = synth.moe_decode_expert_weight(1004, e, N, K)
+        fgg.quantize_blockwise(cuda(we), fgg.Q_E2M1_E8M0_1x32, out=bq[e], scales=be[e])
+        if e in (0, 13, 31):
+            keep[e] = we
+    y = fgg.grouped_gemm_scaled(aq, sa, bq, be, masked_m=cuda(mm), b_qdesc=fgg.Q_E2M1_E8M0_1x32)
+    y2 = fgg.grouped_gemm_scaled(aq, sa, bq, be, masked_m=cuda(mm), b_qdesc=fgg.Q_E2M1_E8M0_1x32)
+    for e in range(G):                     # rows >= masked_m are never written: compare the rest
+        assert torch.equal(y[e, :int(mm[e])], y2[e, :int(mm[e])])
+    y = to_np(y)
+    for e, we in keep.items():
+        m = int(mm[e])
+        aq_r, sa_r = oracle.quantize_e4m3_blocks(wl["x"][e], 1, 128)
+        bc, be_r = oracle.quantize_e2m1_e8m0_groups(we, 32)
+        bp_r = F.pack_e2m1x2(bc)
+        assert np.array_equal(to_np(bq[e]), bp_r)
+        ref = oracle.round_bf16(oracle.grouped_gemm_masked(aq_r[None], sa_r[None], bp_r[None], be_r[None],
+                                                           np.array([m])))
+        tol_check(y[e, :m], ref[0, :m], what=f"decode expert {e}")
+
+
+def test_masked_fp8_equals_contiguous():
+    G, M, N, K = 3, 16, 256, 512
+    x, w, mm = _masked_case(G, M, N, K, 4242, np.array([16, 3, 11], np.int32))
+    aq, sa = _quant_masked_a_gpu(x)
+    bq, sb = _quant_weights_gpu(w, fgg.Q_E4M3_128x128)
+    y_m = to_np(fgg.grouped_gemm_scaled(aq, sa, bq, sb, masked_m=cuda(mm), b_qdesc=fgg.Q_E4M3_128x128))
+    # the same rows laid out contiguously, one 128-row segment per group
+    xc = np.zeros((G * 128, K), np.float32)
+    for e in range(G):
+        xc[e * 128:e * 128 + M] = x[e]
+    xq, xs = fgg.quantize_blockwise(cuda(xc), fgg.Q_E4M3_1x128)
+    y_c = to_np(fgg.grouped_gemm_scaled(xq, xs, bq, sb, offsets=cuda(np.arange(G + 1, dtype=np.int32) * 128)))
+    for e in range(G):
+        m = int(mm[e])
+        assert np.array_equal(y_m[e, :m], y_c[e * 128:e * 128 + m])
+
+
+# ------------------------------------------------------------------- W4A4
+
+def _w4a4_run(wl, rows=None):
+    M, N, K = wl["M"], wl["N"], wl["K"]
+    xq, xs = fgg.quantize_blockwise(cuda(wl["x"]), fgg.Q_E2M1_1x16)
+    wq, ws = fgg.quantize_blockwise(cuda(wl["w"]), fgg.Q_E2M1_1x16)
+    y = fgg.scaled_gemm(xq, xs, wq, ws, qdesc="w4a4", x_bf16=cuda(wl["x"], torch.bfloat16),
+                        l_down=cuda(wl["l_down"], torch.bfloat16), l_up=cuda(wl["l_up"], torch.bfloat16),
+                        bias=cuda(wl["bias"], torch.bfloat16))
+    rows = np.arange(M) if rows is None else rows
+    qx_r, sx_r = oracle.quantize_e2m1_fp32_groups(wl["x"][rows], 16)
+    qw_r, sw_r = oracle.quantize_e2m1_fp32_groups(wl["w"], 16)
+    assert np.array_equal(to_np(xq)[rows], F.pack_e2m1x2(qx_r)) and np.array_equal(to_np(wq), F.pack_e2m1x2(qw_r))
+    ref = oracle.round_bf16(oracle.w4a4_lowrank_gemm(qx_r, sx_r, qw_r, sw_r, wl["x"][rows], wl["l_down"],
+                                                     wl["l_up"], wl["bias"]))
+    return to_np(y)[rows], ref
+
+
+def test_w4a4_small():
+    wl = synth.w4a4(seed=77, M=256, N=384, K=512)
+    y, ref = _w4a4_run(wl)
+    tol_check(y, ref, what="w4a4 small")
+
+
+def test_w4a4_full_size_sampled():
+    wl = synth.w4a4()
+    y, ref = _w4a4_run(wl, rows=np.array([0, 1, 63, 64, 1000, 2048, 4000, 4095]))
+    tol_check(y, ref, what="w4a4 4096x3072x3072 sampled rows")

@@ -1,0 +1,117 @@
+"""GPU parity: moe_permute (bit-exact indices, rows and scales) and
+moe_combine (tolerance; exact for the one-slot unit-weight gather)."""
+
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import fp4_grouped_gemm_amd as fgg
+import oracle
+import synth
+from _util import cuda, to_np, tol_check
+
+pytestmark = pytest.mark.gpu
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _check_permute(ids, E, align=128, K=256, seed=0, m_cap=None):
+    T, k = ids.shape
+    g = synth.rng(seed)
+    xq = g.integers(0, 256, size=(T, K), dtype=np.uint8)
+    xs = g.random((K // 128, T), dtype=np.float32) + np.float32(0.5)       # device layout [K/128, T]
+    got = fgg.moe_permute(cuda(ids), E, align, xq=cuda(xq), xs=cuda(xs), m_cap=m_cap)
+    ref = oracle.moe_permute(ids, E, align)
+    mt = int(ref["offsets"][-1])
+    assert np.array_equal(to_np(got["offsets"]), ref["offsets"])
+    assert np.array_equal(to_np(got["counts"]), ref["counts"])
+    assert np.array_equal(to_np(got["src_to_row"]), ref["src_to_row"])
+    m_cap = got["m_cap"]
+    assert np.array_equal(to_np(got["row_to_src"]), ref["row_to_src"][:m_cap])
+    a_ref, sa_ref = oracle.gather_permuted(ref["row_to_src"], mt, k, xq, xs.T)
+    assert np.array_equal(to_np(got["a"])[:mt], a_ref)
+    assert np.array_equal(to_np(got["sa"])[:, :mt], sa_ref.T)
+    return got, ref
+
+
+def test_permute_two_experts_eight_tokens():
+    d = {}
+    for line in open(os.path.join(GOLDEN, "permute_2x8.txt")):
+        line = line.split("#")[0].strip()
+        if line:
+            key, *vals = line.split()
+            d[key] = [int(v) for v in vals]
+    ids = np.array(d["topk_ids"], dtype=np.int32).reshape(d["T"][0], d["k"][0])
+    got, _ = _check_permute(ids, 2)
+    assert to_np(got["src_to_row"]).tolist() == d["src_to_row"]
+
+
+def test_permute_tiny_moe_routing():
+    w = synth.tiny_moe()
+    _check_permute(w["topk_ids"], 4, K=256, seed=1)
+
+
+@pytest.mark.parametrize("T,k,E,align", [(1, 1, 1, 128), (300, 8, 32, 128), (1000, 6, 17, 128),
+                                         (5000, 4, 256, 128), (777, 3, 5, 16), (70000, 2, 1024, 128)])
+def test_permute_random_with_dropped_ids(T, k, E, align):
+    g = synth.rng(T + k + E)
+    ids = g.integers(-3, E + 3, size=(T, k)).astype(np.int32)
+    _check_permute(ids, E, align, K=128, seed=2)
+
+
+def test_permute_all_dropped_and_one_expert():
+    ids = np.full((64, 4), -1, np.int32)
+    got, ref = _check_permute(ids, 8)
+    assert ref["offsets"][-1] == 0
+    ids = np.zeros((64, 4), np.int32)                    # everything to expert 0
+    _check_permute(ids, 8)
+
+
+def test_permute_moe_prefill_routing_full_size():
+    ids = synth.moe_prefill_routing()["topk_ids"]
+    got, ref = _check_permute(ids, 32, K=7168, seed=3)
+    assert int(ref["offsets"][-1]) == 10112
+
+
+def test_permute_small_m_cap_writes_nothing_beyond():
+    ids = np.zeros((64, 2), np.int32)                    # needs 128 rows
+    g = synth.rng(9)
+    xq = cuda(g.integers(0, 256, size=(64, 128), dtype=np.uint8))
+    xs = cuda(np.ones((1, 64), np.float32))
+    got = fgg.moe_permute(cuda(ids), 2, 128, xq=xq, xs=xs, m_cap=100)
+    assert to_np(got["offsets"]).tolist() == [0, 128, 128]      # the true total is still reported
+    r2s = to_np(got["row_to_src"])
+    assert r2s.shape == (100,) and np.array_equal(r2s, np.arange(100))
+
+
+def test_permute_zero_tokens():
+    ids = np.zeros((0, 4), np.int32)
+    got = fgg.moe_permute(cuda(ids), 3, 128)
+    assert to_np(got["offsets"]).tolist() == [0, 0, 0, 0]
+    assert to_np(got["counts"]).tolist() == [0, 0, 0]
+
+
+@pytest.mark.parametrize("T,k,E,N", [(64, 2, 4, 512), (8192, 8, 32, 7168), (33, 3, 5, 8)])
+def test_combine(T, k, E, N):
+    g = synth.rng(T * 7 + N)
+    ids = g.integers(-1, E, size=(T, k)).astype(np.int32)
+    ref_perm = oracle.moe_permute(ids, E, 128)
+    mt = int(ref_perm["offsets"][-1])
+    y = synth.to_bf16_values(synth.normal(g, (max(mt, 1), N)))
+    w = g.random((T, k)).astype(np.float32)
+    out = fgg.moe_combine(cuda(y, torch.bfloat16), cuda(ref_perm["src_to_row"]), cuda(w))
+    ref = oracle.round_bf16(oracle.moe_combine(y, ref_perm["src_to_row"], w, T, k))
+    tol_check(to_np(out), ref, what="combine")
+    none = np.all(ids < 0, axis=1)
+    assert np.all(to_np(out)[none] == 0)
+
+
+def test_combine_unit_weight_single_slot_is_exact_gather():
+    g = synth.rng(77)
+    T, E, N = 500, 6, 1024
+    ids = g.integers(0, E, size=(T, 1)).astype(np.int32)
+    ref_perm = oracle.moe_permute(ids, E, 128)
+    y = synth.to_bf16_values(synth.normal(g, (int(ref_perm["offsets"][-1]), N)))
+    out = fgg.moe_combine(cuda(y, torch.bfloat16), cuda(ref_perm["src_to_row"]), cuda(np.ones((T, 1), np.float32)))
+    assert np.array_equal(to_np(out), y[ref_perm["src_to_row"]])
