@@ -1,0 +1,335 @@
+#!/usr/bin/env python3
+"""Benchmark of the block-scaled FP8 MoE layer hot path on one MI355X.
+
+One step = one pass of the prefill MoE layer (T=8192 tokens, hidden 7168, 32
+local experts of 256, top-8, Zipf(1.1)-ragged segments padded to 128):
+  quantize X (1x128 e4m3) -> moe_permute -> gate-up grouped GEMM (N=4096)
+  -> SiLU(gate)*up requantized to e4m3 1x128 -> down grouped GEMM (N=7168,
+  K=2048) -> gate-weighted combine (bf16 [8192, 7168]).
+Inputs are resident in HBM before timing starts; expert weights are quantized
+once, untimed (offline weight quantization).
+
+value = useful grouped-GEMM FLOPs of the step (2·8192·(4096·7168 + 7168·2048)
+= 721.6 GFLOP) / measured step time, in TFLOP/s.  The roofline object covers
+the dominant kernel (the gate-up grouped GEMM), timed with HIP events on the
+stream it runs on.  The decode workload (32 experts × 1-16 tokens, FP4
+weights) and the dense / W4A4 shapes are measured in the same run and
+reported under "secondary".
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+METRIC = "grouped-GEMM TFLOPS (% FP8/FP4 MFMA peak); decode GB/s (% HBM peak)"
+PEAK_FP8_TFLOPS = 5000.0     # MI355X dense FP8 MFMA
+PEAK_FP4_TFLOPS = 10100.0    # MI355X dense FP4 MFMA
+PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
+
+
+def _sync():
+    import torch
+    torch.cuda.synchronize()
+
+
+class EventTimer:
+    """Accumulates the device time of one launch site, with events recorded on
+    the current stream (the stream the library's kernels are enqueued on)."""
+
+    def __init__(self):
+        self.pairs = []
+
+    def start(self):
+        import torch
+        e = torch.cuda.Event(enable_timing=True)
+        e.record()
+        self.pairs.append([e, None])
+
+    def stop(self):
+        import torch
+        e = torch.cuda.Event(enable_timing=True)
+        e.record()
+        self.pairs[-1][1] = e
+
+    def mean_ms(self):
+        return float(np.mean([a.elapsed_time(b) for a, b in self.pairs])) if self.pairs else float("nan")
+
+    def reset(self):
+        self.pairs = []
+
+
+# ----------------------------------------------------------------- prefill
+
+def setup_prefill(fgg, synth, torch):
+    cfg = synth.MOE_PREFILL
+    T, K, E, k = cfg["T"], cfg["K"], cfg["E"], cfg["k"]
+    Ngu, Ndn, Kdn = cfg["N_gu"], cfg["N_dn"], cfg["K_dn"]
+    r = synth.moe_prefill_routing()
+    ids = torch.from_numpy(r["topk_ids"]).cuda()
+    tw = torch.from_numpy(r["topk_w"]).cuda()
+    x = torch.from_numpy(synth.moe_prefill_x()).cuda().to(torch.bfloat16)     # layer input, bf16
+    gu_q = torch.empty((E, Ngu, K), dtype=torch.uint8, device="cuda")
+    gu_s = torch.empty((E, Ngu // 128, K // 128), dtype=torch.float32, device="cuda")
+    dn_q = torch.empty((E, Ndn, Kdn), dtype=torch.uint8, device="cuda")
+    dn_s = torch.empty((E, Ndn // 128, Kdn // 128), dtype=torch.float32, device="cuda")
+    for e in range(E):      # offline weight quantization (untimed)
+        w = synth.normal_cuda(31_000 + e, (Ngu, K), 0.02)
+        fgg.quantize_blockwise(w, fgg.Q_E4M3_128x128, out=gu_q[e], scales=gu_s[e])
+        w = synth.normal_cuda(32_000 + e, (Ndn, Kdn), 0.02)
+        fgg.quantize_blockwise(w, fgg.Q_E4M3_128x128, out=dn_q[e], scales=dn_s[e])
+    del w
+    perm = fgg.moe_permute_outputs(T, k, E, 128, K)
+    m_cap = perm["m_cap"]
+    bufs = dict(
+        xq=torch.empty((T, K), dtype=torch.uint8, device="cuda"),
+        xs=torch.empty((K // 128, T), dtype=torch.float32, device="cuda"),
+        h=torch.empty((m_cap, Ngu), dtype=torch.bfloat16, device="cuda"),
+        a2=torch.empty((m_cap, Kdn), dtype=torch.uint8, device="cuda"),
+        s2=torch.empty((Kdn // 128, m_cap), dtype=torch.float32, device="cuda"),
+        y=torch.empty((m_cap, Ndn), dtype=torch.bfloat16, device="cuda"),
+        out=torch.empty((T, Ndn), dtype=torch.bfloat16, device="cuda"),
+    )
+    useful = 2.0 * int((r["topk_ids"] >= 0).sum()) * (Ngu * K + Ndn * Kdn)
+    return dict(cfg=cfg, ids=ids, tw=tw, x=x, gu_q=gu_q, gu_s=gu_s, dn_q=dn_q, dn_s=dn_s, perm=perm,
+                bufs=bufs, useful_flops=useful, routing=r)
+
+
+def prefill_step(fgg, st, t_gu=None, t_dn=None):
+    b, p = st["bufs"], st["perm"]
+    E = st["cfg"]["E"]
+    fgg.quantize_blockwise(st["x"], fgg.Q_E4M3_1x128, out=b["xq"], scales=b["xs"])
+    fgg.moe_permute(st["ids"], E, 128, xq=b["xq"], xs=b["xs"], out=p)
+    if t_gu:
+        t_gu.start()
+    fgg.grouped_gemm_scaled(p["a"], p["sa"], st["gu_q"], st["gu_s"], offsets=p["offsets"], out=b["h"])
+    if t_gu:
+        t_gu.stop()
+    fgg.quantize_blockwise(b["h"], fgg.Q_E4M3_1x128, silu_mul=True, out=b["a2"], scales=b["s2"],
+                           rows_dev=p["offsets"][E:])
+    if t_dn:
+        t_dn.start()
+    fgg.grouped_gemm_scaled(b["a2"], b["s2"], st["dn_q"], st["dn_s"], offsets=p["offsets"], out=b["y"])
+    if t_dn:
+        t_dn.stop()
+    fgg.moe_combine(b["y"], p["src_to_row"], st["tw"], out=b["out"])
+
+
+# ------------------------------------------------------------ secondaries
+
+def time_calls(fn, iters, warmup):
+    import torch
+    for _ in range(warmup):
+        fn(0)
+    _sync()
+    evs = []
+    for i in range(iters):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn(i)
+        b.record()
+        evs.append((a, b))
+    _sync()
+    return float(np.median([a.elapsed_time(b) for a, b in evs]))
+
+
+def bench_decode(fgg, synth, torch, iters=50, copies=3):
+    wl = synth.moe_decode(with_weights=False)
+    G, M, N, K = wl["G"], wl["M_max"], wl["N"], wl["K"]
+    aq, sa = fgg.quantize_blockwise(torch.from_numpy(wl["x"].reshape(G * M, K)).cuda(), fgg.Q_E4M3_1x128)
+    sa = sa.reshape(K // 128, G, M).permute(1, 0, 2).contiguous()
+    aq = aq.reshape(G, M, K)
+    mm = torch.from_numpy(wl["masked_m"]).cuda()
+    bqs, bes = [], []
+    for c in range(copies):       # distinct copies so that caches cannot serve repeats
+        bq = torch.empty((G, N, K // 2), dtype=torch.uint8, device="cuda")
+        be = torch.empty((G, N, K // 32), dtype=torch.uint8, device="cuda")
+        for e in range(G):
+            w = synth.normal_cuda(41_000 + 100 * c + e, (N, K), 0.02)
+            fgg.quantize_blockwise(w, fgg.Q_E2M1_E8M0_1x32, out=bq[e], scales=be[e])
+        bqs.append(bq)
+        bes.append(be)
+    d = torch.empty((G, M, N), dtype=torch.bfloat16, device="cuda")
+    ms = time_calls(lambda i: fgg.grouped_gemm_scaled(aq, sa, bqs[i % copies], bes[i % copies], masked_m=mm,
+                                                      b_qdesc=fgg.Q_E2M1_E8M0_1x32, out=d), iters, 5)
+    wbytes = G * N * (K // 2) + G * N * (K // 32)
+    gbs = wbytes / (ms * 1e-3) / 1e9
+    return dict(workload="moe_decode G=32 M=1..16 (U) N=4096 K=7168 E2M1+E8M0/32 weights, e4m3 1x128 acts",
+                us_per_call=round(ms * 1e3, 2), weight_bytes=wbytes, value=round(gbs, 1), unit="GB/s",
+                pct_hbm_peak=round(100 * gbs / PEAK_HBM_GBS, 1))
+
+
+def bench_dense(fgg, synth, torch, iters=30, copies=3):
+    M = N = 4096
+    K = 7168
+    xq, xs = fgg.quantize_blockwise(synth.normal_cuda(51_000, (M, K)), fgg.Q_E4M3_1x128)
+    ws = [fgg.quantize_blockwise(synth.normal_cuda(51_001 + c, (N, K), 0.02), fgg.Q_E4M3_128x128)
+          for c in range(copies)]
+    d = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    ms = time_calls(lambda i: fgg.scaled_gemm(xq, xs, ws[i % copies][0], ws[i % copies][1], out=d), iters, 5)
+    tf = 2.0 * M * N * K / (ms * 1e-3) / 1e12
+    return dict(workload="dense 4096x4096x7168 e4m3 1x128 / 128x128", us_per_call=round(ms * 1e3, 2),
+                value=round(tf, 1), unit="TFLOP/s", pct_fp8_peak=round(100 * tf / PEAK_FP8_TFLOPS, 1))
+
+
+def bench_w4a4(fgg, synth, torch, iters=30):
+    M, N, K, r = 4096, 3072, 3072, 32
+    x = synth.normal_cuda(61_000, (M, K)).to(torch.bfloat16)
+    xq, xs = fgg.quantize_blockwise(x, fgg.Q_E2M1_1x16)
+    wq, wsc = fgg.quantize_blockwise(synth.normal_cuda(61_001, (N, K), 0.02), fgg.Q_E2M1_1x16)
+    ld = synth.normal_cuda(61_002, (K, r), 0.01).to(torch.bfloat16)
+    lu = synth.normal_cuda(61_003, (r, N), 0.01).to(torch.bfloat16)
+    bias = synth.normal_cuda(61_004, (N,), 0.1).to(torch.bfloat16)
+    d = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(M * r * 2, dtype=torch.uint8, device="cuda")
+    ms = time_calls(lambda i: fgg.scaled_gemm(xq, xs, wq, wsc, qdesc="w4a4", x_bf16=x, l_down=ld, l_up=lu,
+                                              bias=bias, out=d, workspace=ws), iters, 5)
+    flops = 2.0 * M * N * K + 2.0 * M * r * (K + N)
+    tf = flops / (ms * 1e-3) / 1e12
+    return dict(workload="w4a4 4096x3072x3072 E2M1 fp32/16 + rank-32 + bias", us_per_call=round(ms * 1e3, 2),
+                value=round(tf, 1), unit="TFLOP/s", mfu_fp4_pct=round(100 * tf / PEAK_FP4_TFLOPS, 2))
+
+
+# ----------------------------------------------------------- CPU baseline
+
+def cpu_baseline(synth, target_s=12.0):
+    """The oracle's gate-up grouped GEMM (fp64 per-group formula) on the
+    segments of the largest experts of the same routing, added expert by
+    expert until about target_s seconds of CPU work."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    cfg = synth.MOE_PREFILL
+    K, N = cfg["K"], cfg["N_gu"]
+    r = synth.moe_prefill_routing()
+    ids = r["topk_ids"]
+    counts = np.bincount(ids[ids >= 0], minlength=cfg["E"])
+    order = np.argsort(-counts, kind="stable")
+    x = synth.moe_prefill_x()
+    flops = 0.0
+    elapsed = 0.0
+    rows_done = 0
+    used = []
+    for e in order:
+        toks = np.flatnonzero(np.any(ids == e, axis=1))
+        aq, sa = oracle.quantize_e4m3_blocks(x[toks], 1, 128)
+        w = synth.moe_prefill_expert_weight(1003, "gu", int(e), N, K)
+        bq, sb = oracle.quantize_e4m3_blocks(w, 128, 128)
+        t0 = time.perf_counter()
+        oracle.grouped_gemm_contiguous(aq, sa, bq[None], sb[None], np.array([0, len(toks)]))
+        elapsed += time.perf_counter() - t0
+        flops += 2.0 * len(toks) * N * K
+        rows_done += len(toks)
+        used.append(int(e))
+        if elapsed >= target_s:
+            break
+    return {"value": round(flops / elapsed / 1e12, 5), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"oracle gate-up grouped GEMM (fp64 per-group formula) on the {len(used)} largest experts' "
+                      f"segments: {rows_done} rows x N={N} x K={K}, {flops / 1e9:.1f} GFLOP in {elapsed:.1f} s"}
+
+
+# ------------------------------------------------------------------- main
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures the single-GPU path only (one MI355X); there is no multi-GPU mode: "
+              "run it with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+    import fp4_grouped_gemm_amd as fgg
+    import synth
+
+    fgg.load_library()
+    dev = torch.cuda.get_device_properties(0)
+    st = setup_prefill(fgg, synth, torch)
+    _sync()
+
+    for _ in range(args.warmup):
+        prefill_step(fgg, st)
+    _sync()
+    t_gu, t_dn = EventTimer(), EventTimer()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        prefill_step(fgg, st, t_gu, t_dn)
+    _sync()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+    gu_ms, dn_ms = t_gu.mean_ms(), t_dn.mean_ms()
+
+    useful = st["useful_flops"]
+    value = useful / (ms_step * 1e-3) / 1e12
+    cfg = st["cfg"]
+    n_local = int((st["routing"]["topk_ids"] >= 0).sum())
+    gu_flops = 2.0 * n_local * cfg["N_gu"] * cfg["K"]
+    dn_flops = 2.0 * n_local * cfg["N_dn"] * cfg["K_dn"]
+    gu_tf = gu_flops / (gu_ms * 1e-3) / 1e12
+    m_total = int(st["perm"]["offsets"][cfg["E"]].item())
+    result = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3",
+        "data": "synthetic",
+        "config": {
+            "workload": "moe_prefill: T=8192 tokens, K=7168, 32 local experts of 256, top-8, Zipf(1.1) "
+                        "segments padded to 128 (M_total=%d), gate-up N=4096, SiLU*up e4m3 requant, down N=7168 "
+                        "K=2048, combine; e4m3 1x128 activations, 128x128 weights, bf16 out" % m_total,
+            "global_batch": cfg["T"],
+            "parallelism": "single GPU (one expert-parallel shard)",
+            "device": dev.name,
+        },
+        "pct_fp8_peak": round(100 * value / PEAK_FP8_TFLOPS, 2),
+        "gemm_only": {
+            "gate_up_us": round(gu_ms * 1e3, 2), "down_us": round(dn_ms * 1e3, 2),
+            "tflops": round((gu_flops + dn_flops) / ((gu_ms + dn_ms) * 1e-3) / 1e12, 1),
+            "useful_gflop": round((gu_flops + dn_flops) / 1e9, 1),
+        },
+        "roofline": {
+            "kernel": "gemm_fp8_contig_kernel (gate-up grouped GEMM)",
+            "bound": "mfma",
+            "achieved": round(gu_tf, 1),
+            "peak": PEAK_FP8_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(gu_tf / PEAK_FP8_TFLOPS, 4),
+            "traffic": None,
+            "algorithmic": "2*8192*4096*7168 = %.1f GFLOP per launch" % (gu_flops / 1e9),
+        },
+    }
+    if not args.no_secondary:
+        result["secondary"] = {
+            "moe_decode": bench_decode(fgg, synth, torch),
+            "dense": bench_dense(fgg, synth, torch),
+            "w4a4": bench_w4a4(fgg, synth, torch),
+        }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(synth, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

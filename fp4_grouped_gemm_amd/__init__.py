@@ -15,7 +15,8 @@ import torch
 __all__ = [
     "FggError", "load_library", "library_path",
     "Q_E4M3_1x128", "Q_E4M3_128x128", "Q_E2M1_1x16", "Q_E2M1_E8M0_1x32",
-    "quantize_blockwise", "moe_permute", "moe_permute_workspace_bytes", "grouped_gemm_scaled",
+    "quantize_blockwise", "moe_permute", "moe_permute_outputs", "moe_permute_workspace_bytes",
+    "grouped_gemm_scaled",
     "scaled_gemm", "moe_combine", "set_num_cus",
 ]
 
@@ -71,7 +72,7 @@ def load_library():
         "fgg_status_string": ([I32], ctypes.c_char_p),
         "fgg_last_hip_error": ([], I32),
         "fgg_set_num_cus": ([ctypes.c_int], I32),
-        "fgg_quantize_blockwise": ([P, I32, I64, I64, I64, I32, QDesc, P, P, P], I32),
+        "fgg_quantize_blockwise": ([P, I32, I64, I64, I64, I32, QDesc, P, P, P, P], I32),
         "fgg_moe_permute_workspace": ([I64, I32, I32, ctypes.POINTER(SZ)], I32),
         "fgg_moe_permute": ([P, I64, I32, I32, I32, P, P, I64, P, P, P, P, P, P, I64, P, SZ, P], I32),
         "fgg_grouped_gemm_scaled": ([I32, I32, I64, I64, I64, P, P, QDesc, P, P, QDesc, P, P, P, I64, P], I32),
@@ -111,10 +112,13 @@ def set_num_cus(n: int) -> None:
 
 # ------------------------------------------------------------------ quantize
 
-def quantize_blockwise(x: torch.Tensor, qdesc=Q_E4M3_1x128, silu_mul: bool = False, out=None, scales=None):
+def quantize_blockwise(x: torch.Tensor, qdesc=Q_E4M3_1x128, silu_mul: bool = False, out=None, scales=None,
+                       rows_dev=None):
     """Quantize a [rows, cols] fp32/bf16 tensor (rows may have a larger stride).
 
     With silu_mul=True the input has 2·cols columns laid out [gate | up].
+    rows_dev (int32 device tensor, one element) limits the rows processed to
+    min(rows, rows_dev[0]) without a host synchronization.
     Returns (codes, scales) in the layouts of include/fgg.h:
       Q_E4M3_1x128:     codes uint8 [rows, cols],   scales f32 [cols/128, rows]
       Q_E4M3_128x128:   codes uint8 [rows, cols],   scales f32 [rows/128, cols/128]
@@ -139,7 +143,7 @@ def quantize_blockwise(x: torch.Tensor, qdesc=Q_E4M3_1x128, silu_mul: bool = Fal
     xdt = FGG_F32 if x.dtype == torch.float32 else FGG_BF16
     st = load_library().fgg_quantize_blockwise(
         _ptr(x), xdt, rows, cols, x.stride(0), FGG_ACT_SILU_MUL if silu_mul else FGG_ACT_NONE,
-        _q(qdesc), _ptr(out), _ptr(scales), _stream(dev))
+        _q(qdesc), _ptr(rows_dev), _ptr(out), _ptr(scales), _stream(dev))
     _check("fgg_quantize_blockwise", st)
     return out, scales
 
@@ -152,36 +156,49 @@ def moe_permute_workspace_bytes(T: int, k: int, E: int) -> int:
     return n.value
 
 
+def moe_permute_outputs(T: int, k: int, E: int, align: int = 128, K: int = 0, m_cap=None, device="cuda"):
+    """Allocate the output buffers of moe_permute (for reuse across calls)."""
+    if m_cap is None:
+        m_cap = T * k + E * (align - 1)
+    out = dict(
+        offsets=torch.empty(E + 1, dtype=torch.int32, device=device),
+        counts=torch.empty(E, dtype=torch.int32, device=device),
+        src_to_row=torch.empty(max(T * k, 1), dtype=torch.int32, device=device),
+        row_to_src=torch.empty(max(m_cap, 1), dtype=torch.int32, device=device),
+        a=None, sa=None, m_cap=m_cap,
+        workspace=torch.empty(max(moe_permute_workspace_bytes(T, k, E), 1), dtype=torch.uint8, device=device))
+    if K:
+        out["a"] = torch.empty((max(m_cap, 1), K), dtype=torch.uint8, device=device)
+        out["sa"] = torch.empty((K // 128, max(m_cap, 1)), dtype=torch.float32, device=device)
+    return out
+
+
 def moe_permute(topk_ids: torch.Tensor, num_experts: int, align: int = 128, xq=None, xs=None,
-                m_cap=None, workspace=None):
+                m_cap=None, workspace=None, out=None):
     """Stable padded permute.  topk_ids int32 [T, k] on the device.  With xq
     (uint8 [T, K]) and xs (f32 [K/128, T]) the permuted codes/scales are
-    gathered too.  Returns a dict of device tensors (see include/fgg.h)."""
+    gathered too.  Returns a dict of device tensors (see include/fgg.h);
+    ``out`` (from moe_permute_outputs) is filled instead of allocating."""
     assert topk_ids.dtype == torch.int32 and topk_ids.dim() == 2 and topk_ids.is_contiguous()
     T, k = topk_ids.shape
     E = int(num_experts)
     dev = topk_ids.device
-    if m_cap is None:
-        m_cap = T * k + E * (align - 1)
-    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
-    counts = torch.empty(E, dtype=torch.int32, device=dev)
-    s2r = torch.empty(T * k, dtype=torch.int32, device=dev)
-    r2s = torch.empty(max(m_cap, 1), dtype=torch.int32, device=dev)
-    K = 0
-    a_out = sa_out = None
+    K = 0 if xq is None else xq.shape[1]
+    if out is None:
+        out = moe_permute_outputs(T, k, E, align, K, m_cap, dev)
+    m_cap = out["m_cap"]
+    offsets, counts, s2r, r2s = out["offsets"], out["counts"], out["src_to_row"], out["row_to_src"]
+    a_out, sa_out = out["a"], out["sa"]
     if xq is not None:
-        K = xq.shape[1]
         assert xq.dtype == torch.uint8 and xq.is_contiguous() and xs.is_contiguous()
-        a_out = torch.empty((max(m_cap, 1), K), dtype=torch.uint8, device=dev)
-        sa_out = torch.empty((K // 128, max(m_cap, 1)), dtype=torch.float32, device=dev)
-    nbytes = moe_permute_workspace_bytes(T, k, E)
+        assert a_out is not None and a_out.shape[1] == K
     if workspace is None:
-        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+        workspace = out["workspace"]
     st = load_library().fgg_moe_permute(
         _ptr(topk_ids), T, k, E, align, _ptr(xq), _ptr(xs), K, _ptr(offsets), _ptr(counts), _ptr(s2r),
         _ptr(r2s), _ptr(a_out), _ptr(sa_out), m_cap, _ptr(workspace), workspace.numel(), _stream(dev))
     _check("fgg_moe_permute", st)
-    return dict(offsets=offsets, counts=counts, src_to_row=s2r, row_to_src=r2s[:m_cap], a=a_out,
+    return dict(offsets=offsets, counts=counts, src_to_row=s2r[:T * k], row_to_src=r2s[:m_cap], a=a_out,
                 sa=sa_out, m_cap=m_cap)
 
 

@@ -88,7 +88,8 @@ fgg_status fgg_set_num_cus(int n) {
 }
 
 fgg_status fgg_quantize_blockwise(const void* x, fgg_dtype x_dtype, int64_t rows, int64_t cols, int64_t ldx,
-                                  fgg_act act, fgg_qdesc q, void* q_out, void* scales_out, void* stream) {
+                                  fgg_act act, fgg_qdesc q, const int32_t* rows_dev, void* q_out, void* scales_out,
+                                  void* stream) {
   if (rows < 0 || cols < 0) return FGG_ERR_INVALID_VALUE;
   if (x_dtype != FGG_F32 && x_dtype != FGG_BF16) return FGG_ERR_UNSUPPORTED;
   if (act != FGG_ACT_NONE && act != FGG_ACT_SILU_MUL) return FGG_ERR_INVALID_VALUE;
@@ -100,6 +101,7 @@ fgg_status fgg_quantize_blockwise(const void* x, fgg_dtype x_dtype, int64_t rows
   else return FGG_ERR_UNSUPPORTED;
   const bool silu = act == FGG_ACT_SILU_MUL;
   if (silu && kind != fgg::QuantKind::E4M3_1x128) return FGG_ERR_UNSUPPORTED;
+  if (rows_dev && kind != fgg::QuantKind::E4M3_1x128) return FGG_ERR_UNSUPPORTED;
   if (cols % q.block_k != 0) return FGG_ERR_UNSUPPORTED;
   if (q.block_rows == 128 && rows % 128 != 0) return FGG_ERR_UNSUPPORTED;
   if (rows == 0 || cols == 0) return FGG_OK;
@@ -109,10 +111,11 @@ fgg_status fgg_quantize_blockwise(const void* x, fgg_dtype x_dtype, int64_t rows
   const int64_t esz = x_dtype == FGG_F32 ? 4 : 2;
   if (!aligned(x, 16) || (ldx * esz) % 16 != 0 || !aligned(q_out, 16) || !aligned(scales_out, 4))
     return FGG_ERR_INVALID_VALUE;
-  fgg_status st = device_check(nullptr);
+  int num_cus = 0;
+  fgg_status st = device_check(&num_cus);
   if (st != FGG_OK) return st;
-  return finish(fgg::launch_quantize(x, x_dtype == FGG_BF16, rows, cols, ldx, kind, silu, q_out, scales_out,
-                                     (hipStream_t)stream));
+  return finish(fgg::launch_quantize(x, x_dtype == FGG_BF16, rows, cols, ldx, kind, silu, rows_dev, q_out,
+                                     scales_out, num_cus, (hipStream_t)stream));
 }
 
 fgg_status fgg_moe_permute_workspace(int64_t T, int32_t k, int32_t E, size_t* bytes) {

@@ -11,7 +11,8 @@ namespace fgg {
 enum class QuantKind { E4M3_1x128, E4M3_128x128, E2M1_1x16, E2M1_E8M0_1x32 };
 
 hipError_t launch_quantize(const void* x, bool bf16, int64_t rows, int64_t cols, int64_t ldx,
-                           QuantKind kind, bool silu, void* q, void* scales, hipStream_t st);
+                           QuantKind kind, bool silu, const int32_t* rows_dev, void* q, void* scales,
+                           int num_cus, hipStream_t st);
 
 // Permute workspace layout (bytes): hist[nblk][E] int32, base[nblk][E] int32.
 size_t permute_workspace_bytes(int64_t T, int32_t k, int32_t E);

@@ -31,46 +31,57 @@ __device__ inline void load8(const void* base, int64_t idx, float* f) {
 
 // ---------------------------------------------------------------------------
 // 1 x 128 activation groups -> e4m3, scales [cols/128][rows].
-// 16 threads per group (8 elements each); a 256-thread block covers 16 groups.
+// 16 threads per group (8 elements each); a 256-thread block covers 16 groups
+// per step and strides over the groups of rows < min(rows, *rows_dev).
 // SILU: the row holds [gate | up] (2*cols values); a = g / (1 + e^-g) * u.
 template <bool BF16, bool SILU>
 __global__ void __launch_bounds__(256) quant_e4m3_1x128_kernel(const void* __restrict__ x, int64_t rows,
                                                                 int64_t cols, int64_t ldx,
+                                                                const int32_t* __restrict__ rows_dev,
                                                                 uint8_t* __restrict__ q,
                                                                 float* __restrict__ scales) {
   const int64_t nkb = cols / 128;
-  const int64_t group = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
-  const int sub = threadIdx.x & 15;
-  const bool live = group < rows * nkb;
-  const int64_t row = live ? group / nkb : 0;
-  const int64_t kb = live ? group % nkb : 0;
-  const int64_t col = kb * 128 + sub * 8;
-  float v[8];
-  if (live) {
-    load8<BF16>(x, row * ldx + col, v);
-    if (SILU) {
-      float u[8];
-      load8<BF16>(x, row * ldx + cols + col, u);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] = v[i] / (1.0f + expf(-v[i])) * u[i];
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = 0.0f;
+  int64_t live_rows = rows;
+  if (rows_dev) {
+    const int64_t r = *rows_dev;
+    live_rows = r < rows ? (r < 0 ? 0 : r) : rows;
   }
-  float amax = 0.0f;
+  const int64_t ngroups = live_rows * nkb;
+  const int sub = threadIdx.x & 15;
+  for (int64_t g0 = (int64_t)blockIdx.x * 16; g0 < ngroups; g0 += (int64_t)gridDim.x * 16) {
+    const int64_t group = g0 + (threadIdx.x >> 4);
+    const bool live = group < ngroups;
+    const int64_t row = live ? group / nkb : 0;
+    const int64_t kb = live ? group % nkb : 0;
+    const int64_t col = kb * 128 + sub * 8;
+    float v[8];
+    if (live) {
+      load8<BF16>(x, row * ldx + col, v);
+      if (SILU) {
+        float u[8];
+        load8<BF16>(x, row * ldx + cols + col, u);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
-  amax = group_max<16>(amax);
-  const float s = (amax == 0.0f) ? 1.0f : amax / 448.0f;
-  if (!live) return;
-  uint32_t lo = 0, hi = 0;
+        for (int i = 0; i < 8; ++i) v[i] = v[i] / (1.0f + expf(-v[i])) * u[i];
+      }
+    } else {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) lo |= (uint32_t)e4m3_encode(v[i] / s) << (8 * i);
+      for (int i = 0; i < 8; ++i) v[i] = 0.0f;
+    }
+    float amax = 0.0f;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) hi |= (uint32_t)e4m3_encode(v[4 + i] / s) << (8 * i);
-  *reinterpret_cast<uint2*>(q + row * cols + col) = make_uint2(lo, hi);
-  if (sub == 0) scales[kb * rows + row] = s;
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+    amax = group_max<16>(amax);
+    const float s = (amax == 0.0f) ? 1.0f : amax / 448.0f;
+    if (live) {
+      uint32_t lo = 0, hi = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) lo |= (uint32_t)e4m3_encode(v[i] / s) << (8 * i);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) hi |= (uint32_t)e4m3_encode(v[4 + i] / s) << (8 * i);
+      *reinterpret_cast<uint2*>(q + row * cols + col) = make_uint2(lo, hi);
+      if (sub == 0) scales[kb * rows + row] = s;
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -185,18 +196,23 @@ __global__ void __launch_bounds__(256) quant_e2m1_e8m0_1x32_kernel(const void* _
 
 // ---------------------------------------------------------------------------
 hipError_t launch_quantize(const void* x, bool bf16, int64_t rows, int64_t cols, int64_t ldx,
-                           QuantKind kind, bool silu, void* q, void* scales, hipStream_t st) {
+                           QuantKind kind, bool silu, const int32_t* rows_dev, void* q, void* scales,
+                           int num_cus, hipStream_t st) {
   if (rows == 0 || cols == 0) return hipSuccess;
   switch (kind) {
     case QuantKind::E4M3_1x128: {
+      // grid-stride: at most 16 blocks per CU, each block 16 groups per step
       const int64_t groups = rows * (cols / 128);
-      dim3 grid((unsigned)((groups + 15) / 16));
+      int64_t blocks = (groups + 15) / 16;
+      const int64_t cap = (int64_t)(num_cus > 0 ? num_cus : 256) * 16;
+      if (blocks > cap) blocks = cap;
+      dim3 grid((unsigned)blocks);
       if (bf16) {
-        if (silu) hipLaunchKernelGGL((quant_e4m3_1x128_kernel<true, true>), grid, dim3(256), 0, st, x, rows, cols, ldx, (uint8_t*)q, (float*)scales);
-        else hipLaunchKernelGGL((quant_e4m3_1x128_kernel<true, false>), grid, dim3(256), 0, st, x, rows, cols, ldx, (uint8_t*)q, (float*)scales);
+        if (silu) hipLaunchKernelGGL((quant_e4m3_1x128_kernel<true, true>), grid, dim3(256), 0, st, x, rows, cols, ldx, rows_dev, (uint8_t*)q, (float*)scales);
+        else hipLaunchKernelGGL((quant_e4m3_1x128_kernel<true, false>), grid, dim3(256), 0, st, x, rows, cols, ldx, rows_dev, (uint8_t*)q, (float*)scales);
       } else {
-        if (silu) hipLaunchKernelGGL((quant_e4m3_1x128_kernel<false, true>), grid, dim3(256), 0, st, x, rows, cols, ldx, (uint8_t*)q, (float*)scales);
-        else hipLaunchKernelGGL((quant_e4m3_1x128_kernel<false, false>), grid, dim3(256), 0, st, x, rows, cols, ldx, (uint8_t*)q, (float*)scales);
+        if (silu) hipLaunchKernelGGL((quant_e4m3_1x128_kernel<false, true>), grid, dim3(256), 0, st, x, rows, cols, ldx, rows_dev, (uint8_t*)q, (float*)scales);
+        else hipLaunchKernelGGL((quant_e4m3_1x128_kernel<false, false>), grid, dim3(256), 0, st, x, rows, cols, ldx, rows_dev, (uint8_t*)q, (float*)scales);
       }
       break;
     }

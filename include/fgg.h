@@ -113,12 +113,16 @@ fgg_status fgg_set_num_cus(int n);
  *          {E2M1X2,E8M0,1,32}.
  * q_out:   codes, dense [rows][cols] (E4M3) or [rows][cols/2] (E2M1X2).
  * scales_out: in the layout of the quantization kind (see top of file).
+ * rows_dev: optional DEVICE pointer to an int32 row count (e.g. offsets[E] of
+ *          moe_permute); when non-NULL only rows < min(rows, *rows_dev) are
+ *          read and written, so a caller can size `rows` for the worst case
+ *          without a host synchronization.  Only with q = {E4M3, F32, 1, 128}.
  * Requires cols % block_k == 0 and, for 128-row blocks, rows % 128 == 0
  * (else FGG_ERR_UNSUPPORTED).  rows == 0 is a no-op.
  */
 fgg_status fgg_quantize_blockwise(const void* x, fgg_dtype x_dtype, int64_t rows, int64_t cols,
-                                  int64_t ldx, fgg_act act, fgg_qdesc q, void* q_out,
-                                  void* scales_out, void* stream);
+                                  int64_t ldx, fgg_act act, fgg_qdesc q, const int32_t* rows_dev,
+                                  void* q_out, void* scales_out, void* stream);
 
 /*
  * fgg_moe_permute — expert histogram, padded prefix sum and stable scatter.

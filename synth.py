@@ -169,3 +169,15 @@ def w4a4(seed: int = 1005, M: int = 4096, N: int = 3072, K: int = 3072, rank: in
     bias = to_bf16_values(normal(g, (N,), 0.1))
     return dict(M=M, N=N, K=K, rank=rank, x=x, w=w, l_down=l_down, l_up=l_up, bias=bias,
                 outlier_channels=np.sort(outliers))
+
+
+def normal_cuda(seed: int, shape, std: float = 1.0, device: str = "cuda"):
+    """N(0, std) fp32 drawn on the device from torch's seeded generator (used for
+    the large benchmark weight stacks, which are too slow to draw on the host)."""
+    import torch
+    gen = torch.Generator(device=device)
+    gen.manual_seed(int(seed))
+    x = torch.randn(tuple(shape), generator=gen, device=device, dtype=torch.float32)
+    if std != 1.0:
+        x.mul_(std)
+    return x

@@ -54,25 +54,28 @@ def test_quantize_rejects_bad_arguments_on_host():
     P = ctypes.c_void_p
     good = P(4096)
     # negative rows
-    assert lib.fgg_quantize_blockwise(good, fgg.FGG_F32, -1, 128, 128, 0, _q(fgg.Q_E4M3_1x128), good, good, None) == 1
+    assert lib.fgg_quantize_blockwise(good, fgg.FGG_F32, -1, 128, 128, 0, _q(fgg.Q_E4M3_1x128), None, good, good, None) == 1
     # unsupported descriptor
     assert lib.fgg_quantize_blockwise(good, fgg.FGG_F32, 4, 128, 128, 0, _q((fgg.FGG_E4M3, fgg.FGG_F32, 1, 64)),
-                                      good, good, None) == 2
+                                      None, good, good, None) == 2
     # cols not a multiple of the block
-    assert lib.fgg_quantize_blockwise(good, fgg.FGG_F32, 4, 100, 128, 0, _q(fgg.Q_E4M3_1x128), good, good, None) == 2
+    assert lib.fgg_quantize_blockwise(good, fgg.FGG_F32, 4, 100, 128, 0, _q(fgg.Q_E4M3_1x128), None, good, good, None) == 2
     # 128-row blocks with a ragged row count
-    assert lib.fgg_quantize_blockwise(good, fgg.FGG_F32, 100, 128, 128, 0, _q(fgg.Q_E4M3_128x128), good, good,
+    assert lib.fgg_quantize_blockwise(good, fgg.FGG_F32, 100, 128, 128, 0, _q(fgg.Q_E4M3_128x128), None, good, good,
                                       None) == 2
     # SiLU only with the 1x128 e4m3 kind
-    assert lib.fgg_quantize_blockwise(good, fgg.FGG_BF16, 4, 32, 64, 1, _q(fgg.Q_E2M1_E8M0_1x32), good, good,
+    assert lib.fgg_quantize_blockwise(good, fgg.FGG_BF16, 4, 32, 64, 1, _q(fgg.Q_E2M1_E8M0_1x32), None, good, good,
                                       None) == 2
     # null pointers / short leading dimension / misalignment
-    assert lib.fgg_quantize_blockwise(None, fgg.FGG_F32, 4, 128, 128, 0, _q(fgg.Q_E4M3_1x128), good, good, None) == 1
-    assert lib.fgg_quantize_blockwise(good, fgg.FGG_F32, 4, 256, 128, 0, _q(fgg.Q_E4M3_1x128), good, good, None) == 1
-    assert lib.fgg_quantize_blockwise(P(4097), fgg.FGG_F32, 4, 128, 128, 0, _q(fgg.Q_E4M3_1x128), good, good,
-                                      None) == 1
+    assert lib.fgg_quantize_blockwise(None, fgg.FGG_F32, 4, 128, 128, 0, _q(fgg.Q_E4M3_1x128), None, good, good, None) == 1
+    assert lib.fgg_quantize_blockwise(good, fgg.FGG_F32, 4, 256, 128, 0, _q(fgg.Q_E4M3_1x128), None, good, good, None) == 1
+    assert lib.fgg_quantize_blockwise(P(4097), fgg.FGG_F32, 4, 128, 128, 0, _q(fgg.Q_E4M3_1x128), None, good,
+                                      good, None) == 1
+    # the device row limit only with the 1x128 e4m3 kind
+    assert lib.fgg_quantize_blockwise(good, fgg.FGG_F32, 128, 128, 128, 0, _q(fgg.Q_E4M3_128x128), good, good,
+                                      good, None) == 2
     # empty input is a successful no-op even without a device
-    assert lib.fgg_quantize_blockwise(None, fgg.FGG_F32, 0, 128, 128, 0, _q(fgg.Q_E4M3_1x128), None, None, None) == 0
+    assert lib.fgg_quantize_blockwise(None, fgg.FGG_F32, 0, 128, 128, 0, _q(fgg.Q_E4M3_1x128), None, None, None, None) == 0
 
 
 def test_gemm_and_permute_reject_bad_arguments_on_host():

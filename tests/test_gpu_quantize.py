@@ -100,3 +100,20 @@ def test_silu_mul_requant(rows, cols):
         same_sign = (q[mism] & 0x80) == (qr[mism] & 0x80)
         assert np.all(same_sign | (dq[mism] == 0) | (dr[mism] == 0))
         assert np.all(np.abs((q[mism] & 0x7F).astype(int) - (qr[mism] & 0x7F).astype(int)) <= 1)
+
+
+def test_quantize_device_row_limit():
+    x = _input(600, 300, 256, torch.bfloat16, 1.0, specials=False)
+    xt = cuda(x, torch.bfloat16)
+    q = torch.full((300, 256), 0xAB, dtype=torch.uint8, device="cuda")
+    s = torch.full((2, 300), -1.0, dtype=torch.float32, device="cuda")
+    limit = cuda(np.array([123], np.int32))
+    fgg.quantize_blockwise(xt, fgg.Q_E4M3_1x128, out=q, scales=s, rows_dev=limit)
+    qr, sr = oracle.quantize_e4m3_blocks(x[:123], 1, 128)
+    q, s = to_np(q), to_np(s)
+    assert np.array_equal(q[:123], qr) and np.array_equal(s[:, :123], sr.T)
+    assert np.all(q[123:] == 0xAB) and np.all(s[:, 123:] == -1.0)
+    # a limit above `rows` is clamped to `rows`
+    q2, s2 = fgg.quantize_blockwise(xt, fgg.Q_E4M3_1x128, rows_dev=cuda(np.array([10 ** 6], np.int32)))
+    qr2, sr2 = oracle.quantize_e4m3_blocks(x, 1, 128)
+    assert np.array_equal(to_np(q2), qr2) and np.array_equal(to_np(s2), sr2.T)
