@@ -246,6 +246,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one plain 1 GiB device-to-device copy (reference dispatch for HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures the single-GPU path only (one MI355X); there is no multi-GPU mode: "
@@ -261,6 +263,13 @@ def main():
     dev = torch.cuda.get_device_properties(0)
     st = setup_prefill(fgg, synth, torch)
     _sync()
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        _sync()
+        dst.copy_(src)           # reads and writes exactly 1 GiB
+        _sync()
+        del src, dst
 
     for _ in range(args.warmup):
         prefill_step(fgg, st)

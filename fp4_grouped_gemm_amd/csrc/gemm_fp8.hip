@@ -21,7 +21,8 @@
 //    accumulators per lane), two waves per SIMD so that one wave's MFMAs
 //    overlap the other's promotion FMAs, LDS reads and barrier waits; one
 //    workgroup per CU.
-//  * a 3-stage LDS ring (3 x 48.5 KB) filled by global_load_lds_dwordx4, the
+//  * a 3-stage LDS ring (3 x 48.5 KB, K loop unrolled by 3 so every LDS
+//    address is a precomputed lane base plus an immediate) filled by global_load_lds_dwordx4, the
 //    gfx950 direct global->LDS path: no register staging, two K blocks in
 //    flight while the third is consumed ([FP4MoE] §3.2 double-buffered
 //    pipeline; [W4A4] §5 stage index/phase discipline, here a fixed rotation
@@ -35,10 +36,13 @@
 //    c ^ ((r ^ (r >> 3)) & 7) (realized by choosing each lane's source
 //    address, since a DMA instruction writes 1 KB contiguously), keeping the
 //    16-row operand reads free of bank conflicts for 32 and 64 banks.
-//  * persistent grid (one workgroup per CU): each workgroup strides over the
-//    output tiles; a tile's expert is found by binary search over the
-//    segment offsets (segments are multiples of 128 rows, so a tile never
-//    straddles two experts).
+//  * persistent grid (one workgroup per CU), XCD-aware: each XCD's workgroups
+//    take one super-tile of 8 x 4 output tiles per round, so the A and B blocks
+//    they share are fetched once into that XCD's L2; a tile's expert is found
+//    by binary search over the segment offsets (segments are multiples of 128
+//    rows, so a tile never straddles two experts).
+#include <type_traits>
+
 #include "fgg_device.hpp"
 #include "fgg_internal.hpp"
 
@@ -53,16 +57,27 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kWaveCols = BN / kWavesN;          // 64
 constexpr int kNFrag = kWaveCols / 16;           // 4 MFMA column subtiles per wave
 constexpr int kStages = 3;
+constexpr int kXcds = 8;                         // MI355X: 8 accelerator complex dies per device
+constexpr int kSM = 8;                           // super-tile height in M tiles
 constexpr int kABytes = BM * BK;                 // 16 KB
 constexpr int kBBytes = BN * BK;                 // 32 KB
 constexpr int kSBytes = BM * 4;                  // 512 B of activation scales
-constexpr int kStageBytes = kABytes + kBBytes + kSBytes;
+// LDS layout: [A stage 0..2][sA stage 0..2][B stage 0..2], so that the A and sA
+// reads of every stage sit within a 16-bit immediate offset of one base address.
+constexpr int kAOff = 0;
+constexpr int kSOff = kStages * kABytes;
+constexpr int kBOff = kSOff + kStages * kSBytes;
+constexpr int kLdsBytes = kBOff + kStages * kBBytes;
 constexpr int kADma = kABytes / 1024 / kWaves;   // 16-byte-per-lane DMA instructions per wave
 constexpr int kBDma = kBBytes / 1024 / kWaves;
 constexpr int kSRows = BM / kWaves;              // activation scales per wave (dword DMA lanes)
 constexpr int kDmaPerStage = kADma + kBDma + 1;
 
-__device__ inline int swz(int row) { return (row ^ (row >> 3)) & 7; }
+// 16-byte chunk swizzle of a 128-byte LDS row: rows r and r + 16 share a key, so
+// the operand fragments of one lane (rows 16 apart) sit at one base address plus
+// immediates; any 8 consecutive rows, and the 8 even / 8 odd rows of 16
+// consecutive ones, get 8 distinct keys (no bank conflicts for 32 or 64 banks).
+__device__ inline int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 
 // 16 bytes per lane from sbase + voff into LDS at m0 + 16 * lane.
 __device__ inline void dma16(const void* sbase, uint32_t voff, uint32_t lds) {
@@ -97,17 +112,6 @@ __device__ inline void wait_vmcnt() {
 
 __device__ inline void block_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
-__device__ inline v8i read_frag(const uint8_t* tile, int row, int q) {
-  const uint4* base = reinterpret_cast<const uint4*>(tile + row * BK);
-  const int key = swz(row);
-  const uint4 lo = base[(2 * q) ^ key];
-  const uint4 hi = base[(2 * q + 1) ^ key];
-  v8i r;
-  r[0] = (int)lo.x; r[1] = (int)lo.y; r[2] = (int)lo.z; r[3] = (int)lo.w;
-  r[4] = (int)hi.x; r[5] = (int)hi.y; r[6] = (int)hi.z; r[7] = (int)hi.w;
-  return r;
-}
-
 __device__ inline int find_group(const int32_t* __restrict__ offsets, int G, int64_t row) {
   int lo = 0, hi = G - 1;           // largest g with offsets[g] <= row
   while (lo < hi) {
@@ -124,7 +128,7 @@ gemm_fp8_contig_kernel(int G, int64_t M, int64_t N, int64_t K, const uint8_t* __
                        const float* __restrict__ SA, const uint8_t* __restrict__ B,
                        const float* __restrict__ SB, const int32_t* __restrict__ offsets,
                        uint16_t* __restrict__ D, int64_t ldd) {
-  __shared__ __align__(16) uint8_t smem[kStages * kStageBytes];
+  __shared__ __align__(16) uint8_t smem[kLdsBytes];
   const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -135,24 +139,38 @@ gemm_fp8_contig_kernel(int G, int64_t M, int64_t N, int64_t K, const uint8_t* __
   const int64_t m_end = offsets ? (int64_t)offsets[G] : M;
   const int64_t m_tiles = (m_end + BM - 1) / BM;
   const int64_t n_tiles = (N + BN - 1) / BN;     // N % 128 == 0: a last tile may be half wide
-  const int64_t num_tiles = m_tiles * n_tiles;
   const int nkb = (int)(K / BK);
   const int64_t nblk = N / 128;
 
   // DMA lane roles: lane l fills 16-byte LDS chunk (l % 8) of row (l / 8) of an 8-row group;
-  // it reads source chunk (l % 8) ^ swz(row), where swz(row) = (l / 8) ^ (row-group index & 7).
+  // it reads source chunk (l % 8) ^ swz(row), where swz(row) = (l / 8) ^ (row-group index & 1).
   const int lrow = lane >> 3;
   const int lchunk = (lane & 7) ^ lrow;
 
-  for (int64_t tile = blockIdx.x; tile < num_tiles; tile += gridDim.x) {
-    // group 8 M-tiles together, N fastest within the group (operand reuse in L2)
-    const int64_t group_span = 8 * n_tiles;
-    const int64_t grp = tile / group_span;
-    const int64_t first_mt = grp * 8;
-    const int64_t gm = (m_tiles - first_mt) < 8 ? (m_tiles - first_mt) : 8;
-    const int64_t within = tile - grp * group_span;
-    const int64_t mt = first_mt + within % gm;
-    const int64_t nt = within / gm;
+  // Loop-invariant LDS read offsets (stage 0) of this lane's operand fragments:
+  // fragment i is 16 rows (2048 bytes) further, stage s adds s * k{A,S,B}Bytes.
+  const int arow = wm * 64 + l16, brow = wn * kWaveCols + l16;
+  const uint32_t ra_lo = kAOff + arow * BK + (((2 * q) ^ swz(arow)) << 4);
+  const uint32_t ra_hi = kAOff + arow * BK + (((2 * q + 1) ^ swz(arow)) << 4);
+  const uint32_t rb_lo = kBOff + brow * BK + (((2 * q) ^ swz(brow)) << 4);
+  const uint32_t rb_hi = kBOff + brow * BK + (((2 * q + 1) ^ swz(brow)) << 4);
+  const uint32_t rs = kSOff + arow * 4;
+
+  // XCD-aware persistent schedule.  Workgroups are dispatched round-robin over
+  // the 8 XCDs (workgroup b runs on XCD b % 8), each with its own L2.  The tile
+  // grid is cut into super-tiles of kSM x (wg_per_xcd / kSM) tiles; in round r,
+  // XCD x's workgroups cover super-tile 8r + x together, so the operand blocks a
+  // super-tile shares stay in that XCD's L2.
+  const int wg_per_xcd = (int)(gridDim.x / kXcds);
+  const int xcd = (int)(blockIdx.x % kXcds), slot = (int)(blockIdx.x / kXcds);
+  const int sn_tiles = wg_per_xcd / kSM > 0 ? wg_per_xcd / kSM : 1;
+  const int64_t st_m = (m_tiles + kSM - 1) / kSM, st_n = (n_tiles + sn_tiles - 1) / sn_tiles;
+  const int64_t num_st = st_m * st_n;
+  for (int64_t st = xcd; st < num_st; st += kXcds) {
+    if (slot >= kSM * sn_tiles) break;
+    const int64_t mt = (st / st_n) * kSM + slot % kSM;
+    const int64_t nt = (st % st_n) * sn_tiles + slot / kSM;
+    if (mt >= m_tiles || nt >= n_tiles) continue;
     const int64_t m0 = mt * BM, n0 = nt * BN;
     const int g = offsets ? find_group(offsets, G, m0) : 0;
     const int64_t rows_here = (m_end - m0) < BM ? (m_end - m0) : BM;   // >= 1
@@ -170,7 +188,7 @@ gemm_fp8_contig_kernel(int G, int64_t M, int64_t N, int64_t K, const uint8_t* __
     for (int i = 0; i < kADma; ++i) {
       const int grp8 = wave * kADma + i;             // 8-row group of the A tile
       int row = grp8 * 8 + lrow;
-      const int c = lchunk ^ (grp8 & 7);
+      const int c = lchunk ^ (grp8 & 1);
       if (row >= rows_here) row = (int)rows_here - 1;
       offA[i] = (uint32_t)(row * K + c * 16);
     }
@@ -178,7 +196,7 @@ gemm_fp8_contig_kernel(int G, int64_t M, int64_t N, int64_t K, const uint8_t* __
     for (int i = 0; i < kBDma; ++i) {
       const int grp8 = wave * kBDma + i;
       int row = grp8 * 8 + lrow;
-      const int c = lchunk ^ (grp8 & 7);
+      const int c = lchunk ^ (grp8 & 1);
       if (row >= cols_here) row = (int)cols_here - 1;   // half-wide last tile: stay inside B
       offB[i] = (uint32_t)(row * K + c * 16);
     }
@@ -187,16 +205,17 @@ gemm_fp8_contig_kernel(int G, int64_t M, int64_t N, int64_t K, const uint8_t* __
     const uint32_t offS = (uint32_t)(srow * 4);
 
     auto issue = [&](int kb, int stage) {
-      const uint32_t st = lds_base + stage * kStageBytes;
       const uint8_t* a_src = Atile + (int64_t)kb * BK;
       const uint8_t* b_src = Btile + (int64_t)kb * BK;
 #pragma unroll
-      for (int i = 0; i < kADma; ++i) dma16(a_src, offA[i], st + (wave * kADma + i) * 1024);
+      for (int i = 0; i < kADma; ++i)
+        dma16(a_src, offA[i], lds_base + kAOff + stage * kABytes + (wave * kADma + i) * 1024);
 #pragma unroll
-      for (int i = 0; i < kBDma; ++i) dma16(b_src, offB[i], st + kABytes + (wave * kBDma + i) * 1024);
+      for (int i = 0; i < kBDma; ++i)
+        dma16(b_src, offB[i], lds_base + kBOff + stage * kBBytes + (wave * kBDma + i) * 1024);
       // kSRows scales per wave: the first kSRows lanes only (still one DMA instruction per wave)
       const float* s_src = SA + (int64_t)kb * M + m0;
-      if (lane < kSRows) dma4(s_src, offS, st + kABytes + kBBytes + wave * kSRows * 4);
+      if (lane < kSRows) dma4(s_src, offS, lds_base + kSOff + stage * kSBytes + wave * kSRows * 4);
     };
 
     v4f acc[4][kNFrag];
@@ -205,48 +224,103 @@ gemm_fp8_contig_kernel(int G, int64_t M, int64_t N, int64_t K, const uint8_t* __
 #pragma unroll
       for (int j = 0; j < kNFrag; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
+    // Operand fragments of one K block, read from LDS stage ST (a template constant, so
+    // every LDS offset is an immediate).
+    struct Frags {
+      v8i a[4];
+      v8i b[kNFrag];
+      float s[4];
+    };
+    auto load_frags = [&](auto st_tag, Frags& f) {
+      constexpr int ST = decltype(st_tag)::value;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint4 lo = *reinterpret_cast<const uint4*>(smem + ra_lo + ST * kABytes + i * 16 * BK);
+        const uint4 hi = *reinterpret_cast<const uint4*>(smem + ra_hi + ST * kABytes + i * 16 * BK);
+        f.a[i] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        f.s[i] = *reinterpret_cast<const float*>(smem + rs + ST * kSBytes + i * 16 * 4);
+      }
+#pragma unroll
+      for (int j = 0; j < kNFrag; ++j) {
+        const uint4 lo = *reinterpret_cast<const uint4*>(smem + rb_lo + ST * kBBytes + j * 16 * BK);
+        const uint4 hi = *reinterpret_cast<const uint4*>(smem + rb_hi + ST * kBBytes + j * 16 * BK);
+        f.b[j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      }
+    };
+    // 16 MFMAs, each promoted with 4 FMAs.  The promotion of MFMA t is issued after
+    // MFMA t+1, so the matrix core never waits for the vector ALU and the FMAs never
+    // wait for a result that is still in flight; the sched_group_barrier pairs pin
+    // that interleave (1 MFMA, then the 4 FMAs of its predecessor).
+    auto mma = [&](const Frags& f, float sb) {
+      float sab[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sab[i] = f.s[i] * sb;
+      constexpr int T = 4 * kNFrag;
+      v4f p[2];
+      p[0] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(f.b[0], f.a[0], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0,
+                                                             127, 0, 127);
+#pragma unroll
+      for (int t = 1; t <= T; ++t) {
+        if (t < T) {
+          p[t & 1] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              f.b[t % kNFrag], f.a[t / kNFrag], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
+        }
+        const int u = t - 1;
+        const v4f& r = p[u & 1];
+        v4f& c = acc[u / kNFrag][u % kNFrag];
+        const float sc = sab[u / kNFrag];
+        c[0] = fmaf(r[0], sc, c[0]);
+        c[1] = fmaf(r[1], sc, c[1]);
+        c[2] = fmaf(r[2], sc, c[2]);
+        c[3] = fmaf(r[3], sc, c[3]);
+      }
+#pragma unroll
+      for (int t = 0; t < T; ++t) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // 1 MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);   // 4 VALU
+      }
+    };
+
+    // Pipeline.  Stage j lives in LDS buffer j % 3 and is read into registers during
+    // step j - 1, so at the top of step kb buffer kb % 3 is free again: it is refilled
+    // with stage kb + 3 (two steps of DMA lookahead) while the MFMAs of step kb run on
+    // registers and the fragments of stage kb + 1 are read from LDS.
+    //   top of step kb: this wave's DMA of stage kb + 1 done (stage kb + 2 may fly),
+    //   its LDS reads of stage kb done; barrier -> true for all waves.
+    float sb_cur = SBw[0];
+    auto step = [&](auto st_tag, Frags& cur, Frags& nxt, int kb) {
+      constexpr int ST = decltype(st_tag)::value;       // == kb % 3
+      if (kb + 2 < nkb) wait_vmcnt<kDmaPerStage>();
+      else wait_vmcnt<0>();
+      block_barrier();
+      if (kb + 3 < nkb) issue(kb + 3, ST);
+      const float sb_next = SBw[kb + 1 < nkb ? kb + 1 : kb];   // scalar load, used next step
+      if (kb + 1 < nkb) load_frags(std::integral_constant<int, (ST + 1) % kStages>{}, nxt);
+      mma(cur, sb_cur);
+      sb_cur = sb_next;
+    };
+
     block_barrier();          // every wave is done with the previous tile's LDS
     issue(0, 0);
     if (nkb > 1) issue(1, 1);
+    if (nkb > 2) issue(2, 2);
+    if (nkb > 2) wait_vmcnt<2 * kDmaPerStage>();
+    else if (nkb > 1) wait_vmcnt<kDmaPerStage>();
+    else wait_vmcnt<0>();
+    block_barrier();
+    Frags f0, f1;
+    load_frags(std::integral_constant<int, 0>{}, f0);
 
-    for (int kb = 0; kb < nkb; ++kb) {
-      if (kb + 1 < nkb) wait_vmcnt<kDmaPerStage>();   // stage kb landed (kb+1 may still fly)
-      else wait_vmcnt<0>();
-      block_barrier();                                 // ... for all waves; stage (kb+2)%3 is free
-      if (kb + 2 < nkb) issue(kb + 2, (kb + 2) % kStages);
-
-      const int stage = kb % kStages;
-      const uint8_t* At = smem + stage * kStageBytes;
-      const uint8_t* Bt = At + kABytes;
-      const float* St = reinterpret_cast<const float*>(Bt + kBBytes);
-      const float sb = SBw[kb];
-
-      v8i af[4];
-      float sab[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        af[i] = read_frag(At, wm * 64 + 16 * i + l16, q);
-        sab[i] = St[wm * 64 + 16 * i + l16] * sb;
-      }
-#pragma unroll
-      for (int h = 0; h < kNFrag / 4; ++h) {
-        v8i bf[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) bf[j] = read_frag(Bt, wn * kWaveCols + 16 * (4 * h + j) + l16, q);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const v4f p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                bf[j], af[i], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
-            v4f& c = acc[i][4 * h + j];
-            c[0] = fmaf(p[0], sab[i], c[0]);
-            c[1] = fmaf(p[1], sab[i], c[1]);
-            c[2] = fmaf(p[2], sab[i], c[2]);
-            c[3] = fmaf(p[3], sab[i], c[3]);
-          }
-        }
-      }
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    for (int kb = 0; kb < nkb; kb += 6) {
+      step(I0{}, f0, f1, kb);
+      if (kb + 1 < nkb) step(I1{}, f1, f0, kb + 1);
+      if (kb + 2 < nkb) step(I2{}, f0, f1, kb + 2);
+      if (kb + 3 < nkb) step(I0{}, f1, f0, kb + 3);
+      if (kb + 4 < nkb) step(I1{}, f0, f1, kb + 4);
+      if (kb + 5 < nkb) step(I2{}, f1, f0, kb + 5);
     }
 
     // epilogue: lane holds columns n0 + wn*64 + 16j + 4q + (0..3) of row m0 + wm*64 + 16i + l16
@@ -272,10 +346,10 @@ hipError_t launch_gemm_fp8_contig(int32_t G, int64_t M, int64_t N, int64_t K, co
                                   hipStream_t st) {
   if (M == 0 || N == 0) return hipSuccess;
   if (N % 128 != 0 || K % BK != 0) return hipErrorInvalidValue;
-  const int64_t tiles_upper = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+  // one workgroup per CU, a multiple of the XCD count (the schedule assigns tiles per XCD)
   int64_t grid = (int64_t)num_cus;
-  if (grid > tiles_upper) grid = tiles_upper;
-  if (grid < 1) grid = 1;
+  grid = (grid / kXcds) * kXcds;
+  if (grid < kXcds * kSM) grid = kXcds * kSM;
   hipLaunchKernelGGL(gemm_fp8_contig_kernel, dim3((unsigned)grid), dim3(kThreads), 0, st, G, M, N, K, a, sa, b,
                      sb, offsets, d, ldd);
   return hipGetLastError();
