@@ -162,6 +162,7 @@ fgg_status fgg_grouped_gemm_scaled(fgg_layout layout, int32_t G, int64_t M, int6
   int num_cus = 0;
   if (layout == FGG_LAYOUT_CONTIGUOUS) {
     if (!same_q(bq, FGG_E4M3, FGG_F32, 128, 128)) return FGG_ERR_UNSUPPORTED;
+    if (K > 16384) return FGG_ERR_UNSUPPORTED;
     if (!offsets) return FGG_ERR_INVALID_VALUE;
     fgg_status st = device_check(&num_cus);
     if (st != FGG_OK) return st;
@@ -211,6 +212,7 @@ fgg_status fgg_scaled_gemm(int64_t M, int64_t N, int64_t K, const void* a, const
   int num_cus = 0;
   if (same_q(aq, FGG_E4M3, FGG_F32, 1, 128) && same_q(bq, FGG_E4M3, FGG_F32, 128, 128)) {
     if (epi) return FGG_ERR_UNSUPPORTED;
+    if (K > 16384) return FGG_ERR_UNSUPPORTED;
     fgg_status st = device_check(&num_cus);
     if (st != FGG_OK) return st;
     if (M == 0 || N == 0) return FGG_OK;

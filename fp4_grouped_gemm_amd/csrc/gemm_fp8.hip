@@ -67,7 +67,9 @@ constexpr int kSBytes = BM * 4;                  // 512 B of activation scales
 constexpr int kAOff = 0;
 constexpr int kSOff = kStages * kABytes;
 constexpr int kBOff = kSOff + kStages * kSBytes;
-constexpr int kLdsBytes = kBOff + kStages * kBBytes;
+constexpr int kMaxKb = 128;                      // K <= 16384: the tile's weight scales fit one LDS slab
+constexpr int kSBOff = kBOff + kStages * kBBytes;  // [2 column blocks][kMaxKb] fp32 weight scales
+constexpr int kLdsBytes = kSBOff + 2 * kMaxKb * 4;
 constexpr int kADma = kABytes / 1024 / kWaves;   // 16-byte-per-lane DMA instructions per wave
 constexpr int kBDma = kBBytes / 1024 / kWaves;
 constexpr int kSRows = BM / kWaves;              // activation scales per wave (dword DMA lanes)
@@ -104,6 +106,9 @@ __device__ inline void dma4(const void* sbase, uint32_t voff, uint32_t lds) {
       : "v"(voff), "s"(sbase), "s"(lds)
       : "memory");
 }
+
+// s_waitcnt immediate (gfx9 encoding) for lgkmcnt(0) with vmcnt and expcnt left at their maxima
+constexpr int kLgkmZero = 0xC07F;
 
 template <int N>
 __device__ inline void wait_vmcnt() {
@@ -177,9 +182,6 @@ gemm_fp8_contig_kernel(int G, int64_t M, int64_t N, int64_t K, const uint8_t* __
     const int64_t cols_here = (N - n0) < BN ? (N - n0) : BN;           // 128 or 256
     const uint8_t* Atile = A + m0 * K;
     const uint8_t* Btile = B + ((int64_t)g * N + n0) * K;
-    const int64_t nb_w = (n0 + wn * kWaveCols) / 128;
-    const int64_t nb = nb_w < nblk ? nb_w : (nblk - 1);
-    const float* SBw = SB + ((int64_t)g * nblk + nb) * nkb;
 
     // per-lane byte offsets (within the tile) of this wave's DMA rows; rows past the
     // end of A are redirected to the last valid row (their outputs are never stored)
@@ -248,37 +250,43 @@ gemm_fp8_contig_kernel(int G, int64_t M, int64_t N, int64_t K, const uint8_t* __
       }
     };
     // 16 MFMAs, each promoted with 4 FMAs.  The promotion of MFMA t is issued after
-    // MFMA t+1, so the matrix core never waits for the vector ALU and the FMAs never
-    // wait for a result that is still in flight; the sched_group_barrier pairs pin
-    // that interleave (1 MFMA, then the 4 FMAs of its predecessor).
+    // MFMA t+2 (a 2-deep pipeline through three result registers), so the matrix
+    // core never waits for the vector ALU and the FMAs never wait for a result that
+    // is still in flight.  The LDS reads of the next K block's fragments go out in
+    // the first half of the MFMA run (two per MFMA) so that they have landed by the
+    // wait at the top of the next step.  The sched_group_barrier sequence pins this.
     auto mma = [&](const Frags& f, float sb) {
       float sab[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) sab[i] = f.s[i] * sb;
       constexpr int T = 4 * kNFrag;
-      v4f p[2];
-      p[0] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(f.b[0], f.a[0], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0,
-                                                             127, 0, 127);
+      v4f p[3];
 #pragma unroll
-      for (int t = 1; t <= T; ++t) {
+      for (int t = 0; t < T + 2; ++t) {
         if (t < T) {
-          p[t & 1] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+          p[t % 3] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
               f.b[t % kNFrag], f.a[t / kNFrag], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
         }
-        const int u = t - 1;
-        const v4f& r = p[u & 1];
-        v4f& c = acc[u / kNFrag][u % kNFrag];
-        const float sc = sab[u / kNFrag];
-        c[0] = fmaf(r[0], sc, c[0]);
-        c[1] = fmaf(r[1], sc, c[1]);
-        c[2] = fmaf(r[2], sc, c[2]);
-        c[3] = fmaf(r[3], sc, c[3]);
+        if (t >= 2) {
+          const int u = t - 2;
+          const v4f& r = p[u % 3];
+          v4f& c = acc[u / kNFrag][u % kNFrag];
+          const float sc = sab[u / kNFrag];
+          c[0] = fmaf(r[0], sc, c[0]);
+          c[1] = fmaf(r[1], sc, c[1]);
+          c[2] = fmaf(r[2], sc, c[2]);
+          c[3] = fmaf(r[3], sc, c[3]);
+        }
       }
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);     // MFMA 0, 1
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);     // 2 LDS reads
 #pragma unroll
-      for (int t = 0; t < T; ++t) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // 1 MFMA
-        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);   // 4 VALU
+      for (int t = 2; t < T; ++t) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA t
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);   // promotion of MFMA t-2
+        if (t < 10) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // 2 LDS reads
       }
+      __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);     // promotion of the last two
     };
 
     // Pipeline.  Stage j lives in LDS buffer j % 3 and is read into registers during
@@ -287,20 +295,36 @@ gemm_fp8_contig_kernel(int G, int64_t M, int64_t N, int64_t K, const uint8_t* __
     // registers and the fragments of stage kb + 1 are read from LDS.
     //   top of step kb: this wave's DMA of stage kb + 1 done (stage kb + 2 may fly),
     //   its LDS reads of stage kb done; barrier -> true for all waves.
-    float sb_cur = SBw[0];
+    const float* sbl_w = reinterpret_cast<const float*>(smem + kSBOff) + ((wn * kWaveCols) / 128) * kMaxKb;
+    float sb_cur = 0.f;
     auto step = [&](auto st_tag, Frags& cur, Frags& nxt, int kb) {
       constexpr int ST = decltype(st_tag)::value;       // == kb % 3
+      // all of this wave's LDS reads (the fragments of stage kb, the scale) are done:
+      // a real s_waitcnt the compiler sees, so it needs no wait inside the MFMA run
+      __builtin_amdgcn_s_waitcnt(kLgkmZero);
       if (kb + 2 < nkb) wait_vmcnt<kDmaPerStage>();
       else wait_vmcnt<0>();
       block_barrier();
       if (kb + 3 < nkb) issue(kb + 3, ST);
-      const float sb_next = SBw[kb + 1 < nkb ? kb + 1 : kb];   // scalar load, used next step
-      if (kb + 1 < nkb) load_frags(std::integral_constant<int, (ST + 1) % kStages>{}, nxt);
+      // unconditional (the last step's reads are unused but in bounds): keeping the reads
+      // and the MFMAs in one basic block lets the scheduler interleave them
+      load_frags(std::integral_constant<int, (ST + 1) % kStages>{}, nxt);
       mma(cur, sb_cur);
-      sb_cur = sb_next;
+      sb_cur = sbl_w[kb + 1 < nkb ? kb + 1 : kb];      // read now, waited at the next step's top
     };
 
     block_barrier();          // every wave is done with the previous tile's LDS
+    // The tile's weight scales (one 128-column block per wave column pair, all K blocks)
+    // go to LDS once, so the K loop issues no scalar loads: those share lgkmcnt with
+    // the LDS fragment reads and would force a full drain before every promotion.
+    {
+      float* sbl = reinterpret_cast<float*>(smem + kSBOff);
+      for (int t = tid; t < 2 * nkb; t += kThreads) {
+        const int half = t / nkb, kb = t % nkb;
+        const int64_t nbh = (n0 / 128 + half) < nblk ? (n0 / 128 + half) : (nblk - 1);
+        sbl[half * kMaxKb + kb] = SB[((int64_t)g * nblk + nbh) * nkb + kb];
+      }
+    }
     issue(0, 0);
     if (nkb > 1) issue(1, 1);
     if (nkb > 2) issue(2, 2);
@@ -310,6 +334,7 @@ gemm_fp8_contig_kernel(int G, int64_t M, int64_t N, int64_t K, const uint8_t* __
     block_barrier();
     Frags f0, f1;
     load_frags(std::integral_constant<int, 0>{}, f0);
+    sb_cur = sbl_w[0];
 
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;

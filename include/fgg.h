@@ -180,7 +180,8 @@ fgg_status fgg_moe_permute(const int32_t* topk_ids, int64_t T, int32_t k, int32_
  *   b_scales [G][N][K/32] uint8 (the E8M0 scale multiplies each 32-element
  *   block inside the MFMA); or bq = {E4M3,F32,128,128} as above.
  *   D is [G][M][ldd].
- * d: bf16, row stride ldd >= N.  N % 128 == 0, K % 128 == 0, 1 <= G <= 1024.
+ * d: bf16, row stride ldd >= N.  N % 128 == 0, K % 128 == 0, 1 <= G <= 1024;
+ * the contiguous layout supports K <= 16384.
  * Device-side values of offsets / masked_m are trusted within these rules.
  */
 fgg_status fgg_grouped_gemm_scaled(fgg_layout layout, int32_t G, int64_t M, int64_t N, int64_t K,
