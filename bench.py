@@ -32,6 +32,23 @@ PEAK_FP4_TFLOPS = 10100.0    # MI355X dense FP4 MFMA
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
 
 
+def measured_traffic(root):
+    """HBM bytes per launch of the gate-up GEMM from the committed rocprofv3
+    FETCH_SIZE / WRITE_SIZE record, scaled by the copy calibration; None when
+    the kernel's sources changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(root, "profiles", "gemm_fp8_contig_gate_up_traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    h = hashlib.sha256()
+    for s in rec["sources"]:
+        h.update(open(os.path.join(root, s), "rb").read())
+    if h.hexdigest() != rec["sources_sha256"]:
+        return None
+    return (rec["fetch_size_kib"] * rec["fetch_factor"] + rec["write_size_kib"] * rec["write_factor"]) * 1024.0
+
+
 def _sync():
     import torch
     torch.cuda.synchronize()
@@ -325,8 +342,10 @@ def main():
             "peak": PEAK_FP8_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(gu_tf / PEAK_FP8_TFLOPS, 4),
-            "traffic": None,
-            "algorithmic": "2*8192*4096*7168 = %.1f GFLOP per launch" % (gu_flops / 1e9),
+            "traffic": measured_traffic(os.path.dirname(os.path.abspath(__file__))),
+            "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE x2 + WRITE_SIZE, copy-calibrated)",
+            "algorithmic": "2*8192*4096*7168 = %.1f GFLOP per launch; A+B+D = %.0f MB" % (
+                gu_flops / 1e9, (m_total * cfg["K"] + cfg["E"] * cfg["N_gu"] * cfg["K"] + 2 * m_total * cfg["N_gu"]) / 1e6),
         },
     }
     if not args.no_secondary:
