@@ -75,6 +75,7 @@ def load_library():
         "fgg_quantize_blockwise": ([P, I32, I64, I64, I64, I32, QDesc, P, P, P, P], I32),
         "fgg_moe_permute_workspace": ([I64, I32, I32, ctypes.POINTER(SZ)], I32),
         "fgg_moe_permute": ([P, I64, I32, I32, I32, P, P, I64, P, P, P, P, P, P, I64, P, SZ, P], I32),
+        "fgg_moe_permute_quantize": ([P, I64, I32, I32, I32, P, I32, I64, I64, P, P, P, P, P, P, I64, P, SZ, P], I32),
         "fgg_grouped_gemm_scaled": ([I32, I32, I64, I64, I64, P, P, QDesc, P, P, QDesc, P, P, P, I64, P], I32),
         "fgg_scaled_gemm_workspace": ([I64, I64, I64, QDesc, QDesc, ctypes.POINTER(Epilogue), ctypes.POINTER(SZ)], I32),
         "fgg_scaled_gemm": ([I64, I64, I64, P, P, QDesc, P, P, QDesc, ctypes.POINTER(Epilogue), P, I64, P, SZ, P], I32),
@@ -174,15 +175,36 @@ def moe_permute_outputs(T: int, k: int, E: int, align: int = 128, K: int = 0, m_
 
 
 def moe_permute(topk_ids: torch.Tensor, num_experts: int, align: int = 128, xq=None, xs=None,
-                m_cap=None, workspace=None, out=None):
+                m_cap=None, workspace=None, out=None, x=None):
     """Stable padded permute.  topk_ids int32 [T, k] on the device.  With xq
     (uint8 [T, K]) and xs (f32 [K/128, T]) the permuted codes/scales are
-    gathered too.  Returns a dict of device tensors (see include/fgg.h);
-    ``out`` (from moe_permute_outputs) is filled instead of allocating."""
+    gathered too.  With x (bf16 or f32 [T, K], unit column stride) instead,
+    the 1x128 e4m3 quantization is fused into the gather
+    (fgg_moe_permute_quantize; same outputs as quantizing first).  Returns a
+    dict of device tensors (see include/fgg.h); ``out`` (from
+    moe_permute_outputs) is filled instead of allocating."""
     assert topk_ids.dtype == torch.int32 and topk_ids.dim() == 2 and topk_ids.is_contiguous()
     T, k = topk_ids.shape
     E = int(num_experts)
     dev = topk_ids.device
+    if x is not None:
+        assert xq is None and x.dim() == 2 and x.shape[0] == T and x.stride(1) == 1
+        assert x.dtype in (torch.bfloat16, torch.float32)
+        K = x.shape[1]
+        if out is None:
+            out = moe_permute_outputs(T, k, E, align, K, m_cap, dev)
+        assert out["a"] is not None and out["a"].shape[1] == K
+        if workspace is None:
+            workspace = out["workspace"]
+        st = load_library().fgg_moe_permute_quantize(
+            _ptr(topk_ids), T, k, E, align, _ptr(x), FGG_BF16 if x.dtype == torch.bfloat16 else FGG_F32, K,
+            x.stride(0), _ptr(out["offsets"]), _ptr(out["counts"]), _ptr(out["src_to_row"]),
+            _ptr(out["row_to_src"]), _ptr(out["a"]), _ptr(out["sa"]), out["m_cap"], _ptr(workspace),
+            workspace.numel(), _stream(dev))
+        _check("fgg_moe_permute_quantize", st)
+        m = out["m_cap"]
+        return dict(offsets=out["offsets"], counts=out["counts"], src_to_row=out["src_to_row"][:T * k],
+                    row_to_src=out["row_to_src"][:m], a=out["a"], sa=out["sa"], m_cap=m)
     K = 0 if xq is None else xq.shape[1]
     if out is None:
         out = moe_permute_outputs(T, k, E, align, K, m_cap, dev)

@@ -148,6 +148,30 @@ fgg_status fgg_moe_permute(const int32_t* topk_ids, int64_t T, int32_t k, int32_
                                     (hipStream_t)stream));
 }
 
+fgg_status fgg_moe_permute_quantize(const int32_t* topk_ids, int64_t T, int32_t k, int32_t E, int32_t align,
+                                    const void* x, fgg_dtype x_dtype, int64_t K, int64_t ldx, int32_t* offsets,
+                                    int32_t* counts, int32_t* src_to_row, int32_t* row_to_src, void* a_out,
+                                    float* sa_out, int64_t M_cap, void* workspace, size_t ws_bytes, void* stream) {
+  if (T < 0 || k < 1 || k > 64 || E < 1 || E > 1024 || align < 1 || align > 1024 || M_cap < 0 || K < 0)
+    return FGG_ERR_INVALID_VALUE;
+  if (x_dtype != FGG_BF16 && x_dtype != FGG_F32) return FGG_ERR_UNSUPPORTED;
+  if (K == 0 || K % 128 != 0) return FGG_ERR_UNSUPPORTED;
+  if (!offsets || !counts) return FGG_ERR_INVALID_VALUE;
+  if (T > 0 && (!topk_ids || !src_to_row || !x)) return FGG_ERR_INVALID_VALUE;
+  if (M_cap > 0 && (!row_to_src || !a_out || !sa_out)) return FGG_ERR_INVALID_VALUE;
+  if (T * (int64_t)k > (int64_t)INT32_MAX || M_cap > (int64_t)INT32_MAX) return FGG_ERR_UNSUPPORTED;
+  const int64_t esz = x_dtype == FGG_F32 ? 4 : 2;
+  if (T > 0 && (ldx < K || !aligned(x, 16) || (ldx * esz) % 16 != 0)) return FGG_ERR_INVALID_VALUE;
+  if (M_cap > 0 && (!aligned(a_out, 16) || !aligned(sa_out, 4))) return FGG_ERR_INVALID_VALUE;
+  if (T > 0 && (!workspace || ws_bytes < fgg::permute_workspace_bytes(T, k, E))) return FGG_ERR_INVALID_VALUE;
+  int num_cus = 0;
+  fgg_status st = device_check(&num_cus);
+  if (st != FGG_OK) return st;
+  return finish(fgg::launch_permute_quantize(topk_ids, T, k, E, align, x, x_dtype == FGG_BF16, K, ldx, offsets,
+                                             counts, src_to_row, row_to_src, (uint8_t*)a_out, sa_out, M_cap,
+                                             workspace, num_cus, (hipStream_t)stream));
+}
+
 fgg_status fgg_grouped_gemm_scaled(fgg_layout layout, int32_t G, int64_t M, int64_t N, int64_t K,
                                    const void* a, const void* a_scales, fgg_qdesc aq, const void* b,
                                    const void* b_scales, fgg_qdesc bq, const int32_t* offsets,

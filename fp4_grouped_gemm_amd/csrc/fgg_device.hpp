@@ -61,6 +61,48 @@ __host__ __device__ inline uint32_t e2m1_encode(float v) {
   return sign | c;
 }
 
+// fl32(x / s) as far as the e4m3 code of it is concerned, given r = rcp(s).
+// One Newton step after the reciprocal product leaves q within one ulp of the
+// correctly rounded quotient.  That neighbourhood can change the e4m3 code only
+// when q sits within a few ulps of a rounding midpoint (the 20 bits below the
+// 3 kept mantissa bits near 0x80000), below the normal e4m3 range (a finer
+// grid), or far above 448 / not finite (degenerate scales); those lanes take
+// the IEEE division, every other lane's code equals that of the exact quotient.
+// Requires s > 0.
+__device__ inline float e4m3_quotient(float x, float s, float r) {
+  float q = x * r;
+  const float e = __builtin_fmaf(-q, s, x);
+  q = __builtin_fmaf(e, r, q);
+  const uint32_t a = __float_as_uint(q) & 0x7FFFFFFFu;
+  const bool risky = (a - 1u < 0x3C7FFFFFu) | ((a & 0xFFFFFu) - 0x7FFFDu < 7u) | (a > 0x43E80000u);
+  if (__builtin_expect(risky, 0)) q = x / s;
+  // s > 0, so the quotient carries x's sign; the correction step turns -0 into +0
+  return __builtin_copysignf(q, x);
+}
+
+// Four e4m3 codes packed little-endian (v0 in the low byte), by the gfx950
+// conversion instruction (OCP e4m3, round to nearest even) after clamping to
+// the finite range; equal to e4m3_encode on every finite input.
+__device__ inline uint32_t e4m3_pack4(float v0, float v1, float v2, float v3) {
+  v0 = __builtin_amdgcn_fmed3f(v0, -448.0f, 448.0f);
+  v1 = __builtin_amdgcn_fmed3f(v1, -448.0f, 448.0f);
+  v2 = __builtin_amdgcn_fmed3f(v2, -448.0f, 448.0f);
+  v3 = __builtin_amdgcn_fmed3f(v3, -448.0f, 448.0f);
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(v0, v1, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(v2, v3, w, true);
+  return (uint32_t)w;
+}
+
+// a / d for d >= 1 (SiLU denominators): reciprocal and one Newton step,
+// within about one ulp; d is clamped finite so that a huge denominator gives 0.
+__device__ inline float div_by_ge1(float a, float d) {
+  d = __builtin_fminf(d, 3.0e38f);
+  const float r = __builtin_amdgcn_rcpf(d);
+  float t = a * r;
+  const float e = __builtin_fmaf(-t, d, a);
+  return __builtin_fmaf(e, r, t);
+}
+
 // fp32 -> bf16 bits, round to nearest even (NaN stays NaN).
 __host__ __device__ inline uint16_t bf16_bits_rne(float v) {
   uint32_t b;
@@ -89,6 +131,25 @@ __device__ inline float group_max(float v) {
 #pragma unroll
   for (int o = W / 2; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, W));
   return v;
+}
+
+// Eight consecutive elements (bf16 or fp32) as fp32, from 16- or 32-byte loads.
+template <bool BF16>
+__device__ inline void load8(const void* base, int64_t idx, float* f) {
+  if (BF16) {
+    const uint4 u = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(base) + idx);
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = bf16_to_f32((uint16_t)(w[i] & 0xFFFFu));
+      f[2 * i + 1] = bf16_to_f32((uint16_t)(w[i] >> 16));
+    }
+  } else {
+    const float4* p = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(base) + idx);
+    const float4 a = p[0], b = p[1];
+    f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
+    f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+  }
 }
 
 }  // namespace fgg

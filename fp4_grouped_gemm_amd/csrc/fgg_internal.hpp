@@ -21,6 +21,10 @@ hipError_t launch_permute(const int32_t* ids, int64_t T, int32_t k, int32_t E, i
                           int32_t* counts, int32_t* src_to_row, int32_t* row_to_src, uint8_t* a_out,
                           float* sa_out, int64_t M_cap, void* ws, hipStream_t st);
 
+hipError_t launch_permute_quantize(const int32_t* ids, int64_t T, int32_t k, int32_t E, int32_t align,
+                                   const void* x, bool bf16, int64_t K, int64_t ldx, int32_t* offsets,
+                                   int32_t* counts, int32_t* src_to_row, int32_t* row_to_src, uint8_t* a_out,
+                                   float* sa_out, int64_t M_cap, void* ws, int num_cus, hipStream_t st);
 hipError_t launch_combine(const uint16_t* y, int64_t ldy, const int32_t* src_to_row, const float* w,
                           int64_t T, int32_t k, int64_t N, uint16_t* out, int64_t ldo,
                           hipStream_t st);

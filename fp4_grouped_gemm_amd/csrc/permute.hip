@@ -9,14 +9,16 @@
 // output is the gate-weighted sum of the selected experts' outputs.
 //
 // Pipeline (all integer work, deterministic):
-//   hist:    block b counts its CHUNK pairs per expert (LDS atomics).
-//   scan:    one block: per expert, exclusive prefix over blocks -> base[b][e];
-//            padded counts -> offsets (exclusive scan over experts).
-//   scatter: block b walks its pairs in order; a pair's rank among equal
-//            experts comes from wave ballots (stable), plus per-wave and
-//            per-block running counts.
-//   gather:  rows [0, M_total) copy their token's codes and scales (zeros
-//            for padding rows).
+//   hist:    block b counts its kChunk pairs per expert (LDS atomics) into
+//            hist[e][b]; the grid also sets row_to_src to -1.
+//   scan:    one block per expert: exclusive prefix of hist[e][*] over blocks,
+//            and the expert's total.
+//   scatter: every block derives the padded segment offsets from the totals
+//            (block 0 publishes them); block b then walks its pairs in order,
+//            a pair's rank among equal experts coming from wave ballots
+//            (stable) plus per-wave and per-block running counts.
+//   gather:  one wave per row of [0, M_total) copies the token's codes (zeros
+//            for padding rows); a second phase writes the K-block-major scales.
 #include "fgg_device.hpp"
 #include "fgg_internal.hpp"
 
@@ -28,13 +30,25 @@ static constexpr int kMaxE = 1024;
 size_t permute_workspace_bytes(int64_t T, int32_t k, int32_t E) {
   const int64_t pairs = T * (int64_t)k;
   const int64_t nblk = (pairs + kChunk - 1) / kChunk;
-  return (size_t)(2 * nblk * (int64_t)E * sizeof(int32_t)) + 256;
+  return (size_t)(nblk * (int64_t)E * sizeof(int32_t)) + 256;
 }
 
 __device__ inline int valid_expert(int e, int E) { return (e >= 0 && e < E) ? e : -1; }
 
+// Inclusive sum over the 64 lanes of a wave.
+__device__ inline int wave_inclusive_sum(int x) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  return x;
+}
+
 __global__ void __launch_bounds__(256) permute_hist_kernel(const int32_t* __restrict__ ids, int64_t pairs,
-                                                            int E, int32_t* __restrict__ hist) {
+                                                            int E, int64_t nblk, int32_t* __restrict__ hist,
+                                                            int32_t* __restrict__ row_to_src, int64_t M_cap) {
   __shared__ int cnt[kMaxE];
   for (int e = threadIdx.x; e < E; e += 256) cnt[e] = 0;
   __syncthreads();
@@ -46,58 +60,76 @@ __global__ void __launch_bounds__(256) permute_hist_kernel(const int32_t* __rest
       if (e >= 0) atomicAdd(&cnt[e], 1);
     }
   }
+  for (int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x; r < M_cap; r += (int64_t)gridDim.x * 256)
+    row_to_src[r] = -1;
   __syncthreads();
-  for (int e = threadIdx.x; e < E; e += 256) hist[(int64_t)blockIdx.x * E + e] = cnt[e];
-}
-
-// One block of 1024 threads; thread e owns expert e.
-__global__ void __launch_bounds__(1024) permute_scan_kernel(int32_t* __restrict__ hist, int64_t nblk, int E,
-                                                             int align, int32_t* __restrict__ offsets,
-                                                             int32_t* __restrict__ counts) {
-  __shared__ int scan[kMaxE];
-  const int e = threadIdx.x;
-  int running = 0;
-  if (e < E) {
-    for (int64_t b = 0; b < nblk; ++b) {
-      const int h = hist[b * E + e];
-      hist[b * E + e] = running;        // exclusive prefix over blocks (made absolute below)
-      running += h;
-    }
-    counts[e] = running;
-  }
-  const int padded = (e < E) ? ((running + align - 1) / align) * align : 0;
-  scan[e] = padded;
-  __syncthreads();
-  // Hillis-Steele inclusive scan over 1024 entries
-  for (int off = 1; off < kMaxE; off <<= 1) {
-    const int v = (e >= off) ? scan[e - off] : 0;
-    __syncthreads();
-    scan[e] += v;
-    __syncthreads();
-  }
-  const int excl = scan[e] - padded;
-  if (e < E) {
-    offsets[e] = excl;
-    for (int64_t b = 0; b < nblk; ++b) hist[b * E + e] += excl;
-  }
-  if (e == E - 1) offsets[E] = scan[e];
+  for (int e = threadIdx.x; e < E; e += 256) hist[(int64_t)e * nblk + blockIdx.x] = cnt[e];
 }
 
 __global__ void __launch_bounds__(256) fill_i32_kernel(int32_t* __restrict__ p, int64_t n, int32_t v) {
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = v;
 }
 
+// Block e: exclusive prefix of hist[e][0..nblk) in place; counts[e] = total.
+__global__ void __launch_bounds__(256) permute_scan_kernel(int32_t* __restrict__ hist, int64_t nblk,
+                                                            int32_t* __restrict__ counts) {
+  __shared__ int wsum[4];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int32_t* h = hist + (int64_t)blockIdx.x * nblk;
+  int carry = 0;
+  for (int64_t b0 = 0; b0 < nblk; b0 += 256) {
+    const int64_t b = b0 + threadIdx.x;
+    const int v = b < nblk ? h[b] : 0;
+    const int incl = wave_inclusive_sum(v);
+    if (lane == 63) wsum[wave] = incl;
+    __syncthreads();
+    int before = carry;
+    for (int w = 0; w < wave; ++w) before += wsum[w];
+    if (b < nblk) h[b] = before + incl - v;
+    carry += wsum[0] + wsum[1] + wsum[2] + wsum[3];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) counts[blockIdx.x] = carry;
+}
+
 __global__ void __launch_bounds__(256) permute_scatter_kernel(const int32_t* __restrict__ ids, int64_t pairs,
-                                                               int E, const int32_t* __restrict__ base,
+                                                               int E, int align, int64_t nblk,
+                                                               const int32_t* __restrict__ hist,
+                                                               const int32_t* __restrict__ counts,
+                                                               int32_t* __restrict__ offsets,
                                                                int32_t* __restrict__ src_to_row,
                                                                int32_t* __restrict__ row_to_src, int64_t M_cap) {
   __shared__ int running[kMaxE];
   __shared__ int wave_cnt[4][kMaxE];
+  __shared__ int wsum[4];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  for (int e = threadIdx.x; e < E; e += 256) {
-    running[e] = base[(int64_t)blockIdx.x * E + e];
-    wave_cnt[0][e] = wave_cnt[1][e] = wave_cnt[2][e] = wave_cnt[3][e] = 0;
+  // Segment offsets: exclusive scan of the padded counts; thread t owns experts 4t..4t+3.
+  {
+    int pc[4], local = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = threadIdx.x * 4 + i;
+      pc[i] = e < E ? ((counts[e] + align - 1) / align) * align : 0;
+      local += pc[i];
+    }
+    const int incl = wave_inclusive_sum(local);
+    if (lane == 63) wsum[wave] = incl;
+    __syncthreads();
+    int run = incl - local;
+    for (int w = 0; w < wave; ++w) run += wsum[w];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = threadIdx.x * 4 + i;
+      if (e < E) {
+        running[e] = run + hist[(int64_t)e * nblk + blockIdx.x];
+        if (blockIdx.x == 0) offsets[e] = run;
+      }
+      run += pc[i];
+    }
+    if (blockIdx.x == 0 && threadIdx.x == 255) offsets[E] = run;
   }
+  for (int e = threadIdx.x; e < E; e += 256)
+    wave_cnt[0][e] = wave_cnt[1][e] = wave_cnt[2][e] = wave_cnt[3][e] = 0;
   __syncthreads();
   const int64_t p0 = (int64_t)blockIdx.x * kChunk;
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
@@ -133,7 +165,9 @@ __global__ void __launch_bounds__(256) permute_scatter_kernel(const int32_t* __r
   }
 }
 
-// Copy each row's token codes (K bytes) and 1x128 scales; zeros for padding.
+// Rows [0, min(offsets[E], M_cap)): one wave per row copies the token's K code
+// bytes (or zeros for a padding row), 8 x 16 B per lane in flight; then the
+// K-block-major scales sa_out[kb][r] with consecutive threads on consecutive r.
 __global__ void __launch_bounds__(256) permute_gather_kernel(const int32_t* __restrict__ offsets, int E, int k,
                                                               const int32_t* __restrict__ row_to_src,
                                                               const uint8_t* __restrict__ xq,
@@ -142,19 +176,148 @@ __global__ void __launch_bounds__(256) permute_gather_kernel(const int32_t* __re
                                                               float* __restrict__ sa_out, int64_t M_cap) {
   int64_t m_total = offsets[E];
   if (m_total > M_cap) m_total = M_cap;
-  const int64_t nkb = K / 128;
-  for (int64_t r = blockIdx.x; r < m_total; r += gridDim.x) {
+  const int lane = threadIdx.x & 63;
+  const int64_t nvec = K / 16;
+  const int64_t wave_id = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t nwaves = (int64_t)gridDim.x * 4;
+  for (int64_t r = wave_id; r < m_total; r += nwaves) {
     const int32_t p = row_to_src[r];
     uint4* dst = reinterpret_cast<uint4*>(a_out + r * K);
     if (p >= 0) {
-      const int64_t t = p / k;
-      const uint4* src = reinterpret_cast<const uint4*>(xq + t * K);
-      for (int64_t i = threadIdx.x; i < K / 16; i += 256) dst[i] = src[i];
-      for (int64_t kb = threadIdx.x; kb < nkb; kb += 256) sa_out[kb * M_cap + r] = xs[kb * T + t];
+      const uint4* src = reinterpret_cast<const uint4*>(xq + (int64_t)(p / k) * K);
+      for (int64_t i0 = lane; i0 < nvec; i0 += 64 * 8) {
+        uint4 v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          if (i0 + 64 * u < nvec) v[u] = src[i0 + 64 * u];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          if (i0 + 64 * u < nvec) dst[i0 + 64 * u] = v[u];
+      }
     } else {
-      for (int64_t i = threadIdx.x; i < K / 16; i += 256) dst[i] = make_uint4(0, 0, 0, 0);
-      for (int64_t kb = threadIdx.x; kb < nkb; kb += 256) sa_out[kb * M_cap + r] = 0.0f;
+      for (int64_t i = lane; i < nvec; i += 64) dst[i] = make_uint4(0, 0, 0, 0);
     }
+  }
+  const int64_t nkb = K / 128;
+  const int64_t n = nkb * m_total;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+    const int64_t kb = i / m_total, r = i - kb * m_total;
+    const int32_t p = row_to_src[r];
+    sa_out[kb * M_cap + r] = p >= 0 ? xs[kb * T + p / k] : 0.0f;
+  }
+}
+
+// Fused quantize + gather: the same outputs as quantizing x to e4m3 with 1x128
+// scales and then gathering the codes (the permute_gather_kernel contract),
+// without writing or re-reading the token-order codes.  One wave per token:
+// lane j < k holds slot j's destination row; a token with no destination
+// below M_cap is not read at all.  The wave walks K in passes of 512 columns
+// (16 lanes x 8 elements per 128-column group), loading up to kPB passes
+// before using them, and writes each pass's codes and scales to every
+// destination row.  A second phase zero-fills the padding rows of [0, M_total).
+template <bool BF16>
+struct RawRow8 {
+  uint4 a, b;   // b only for fp32 input
+};
+
+template <bool BF16>
+__device__ inline RawRow8<BF16> load_raw8(const void* base, int64_t idx) {
+  RawRow8<BF16> r;
+  if (BF16) {
+    r.a = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(base) + idx);
+    r.b = make_uint4(0, 0, 0, 0);
+  } else {
+    const uint4* q = reinterpret_cast<const uint4*>(reinterpret_cast<const float*>(base) + idx);
+    r.a = q[0];
+    r.b = q[1];
+  }
+  return r;
+}
+
+template <bool BF16>
+__device__ inline void unpack_raw8(const RawRow8<BF16>& r, float* f) {
+  if (BF16) {
+    const uint32_t w[4] = {r.a.x, r.a.y, r.a.z, r.a.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = bf16_to_f32((uint16_t)(w[i] & 0xFFFFu));
+      f[2 * i + 1] = bf16_to_f32((uint16_t)(w[i] >> 16));
+    }
+  } else {
+    f[0] = __uint_as_float(r.a.x); f[1] = __uint_as_float(r.a.y);
+    f[2] = __uint_as_float(r.a.z); f[3] = __uint_as_float(r.a.w);
+    f[4] = __uint_as_float(r.b.x); f[5] = __uint_as_float(r.b.y);
+    f[6] = __uint_as_float(r.b.z); f[7] = __uint_as_float(r.b.w);
+  }
+}
+
+template <bool BF16>
+__global__ void __launch_bounds__(256) permute_quantize_kernel(const int32_t* __restrict__ offsets, int E, int k,
+                                                                const int32_t* __restrict__ src_to_row,
+                                                                const int32_t* __restrict__ row_to_src,
+                                                                const void* __restrict__ x, int64_t ldx,
+                                                                int64_t T, int64_t K,
+                                                                uint8_t* __restrict__ a_out,
+                                                                float* __restrict__ sa_out, int64_t M_cap) {
+  constexpr int kPB = 8;   // passes of 512 columns loaded together
+  const int lane = threadIdx.x & 63, sub = lane & 15;
+  const int64_t wave_id = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t nwaves = (int64_t)gridDim.x * 4;
+  for (int64_t t = wave_id; t < T; t += nwaves) {
+    const int32_t dst = lane < k ? src_to_row[t * k + lane] : -1;
+    const uint64_t dmask = __ballot(dst >= 0 && dst < M_cap);
+    if (dmask == 0) continue;
+    for (int64_t c0 = 0; c0 < K; c0 += 512 * kPB) {
+      RawRow8<BF16> raw[kPB];
+#pragma unroll
+      for (int pb = 0; pb < kPB; ++pb) {
+        const int64_t col = c0 + 512 * pb + 8 * lane;
+        if (col < K) raw[pb] = load_raw8<BF16>(x, t * ldx + col);
+      }
+#pragma unroll
+      for (int pb = 0; pb < kPB; ++pb) {
+        const int64_t col = c0 + 512 * pb + 8 * lane;
+        if (c0 + 512 * pb >= K) break;              // wave-uniform
+        const bool live = col < K;                  // uniform per 16-lane group (K % 128 == 0)
+        float v[8];
+        if (live) {
+          unpack_raw8<BF16>(raw[pb], v);
+        } else {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) v[i] = 0.0f;
+        }
+        float amax = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+        amax = group_max<16>(amax);
+        const float s = (amax == 0.0f) ? 1.0f : amax / 448.0f;
+        const float r = __builtin_amdgcn_rcpf(s);
+        float y[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) y[i] = e4m3_quotient(v[i], s, r);
+        const uint2 codes = make_uint2(e4m3_pack4(y[0], y[1], y[2], y[3]), e4m3_pack4(y[4], y[5], y[6], y[7]));
+        const int64_t kb = col >> 7;
+        uint64_t m = dmask;
+        while (m) {
+          const int j = __ffsll((unsigned long long)m) - 1;
+          m &= m - 1;
+          const int64_t row = __shfl(dst, j);
+          if (live) {
+            *reinterpret_cast<uint2*>(a_out + row * K + col) = codes;
+            if (sub == 0) sa_out[kb * M_cap + row] = s;
+          }
+        }
+      }
+    }
+  }
+  int64_t m_total = offsets[E];
+  if (m_total > M_cap) m_total = M_cap;
+  const int64_t nvec = K / 16, nkb = K / 128;
+  for (int64_t r = wave_id; r < m_total; r += nwaves) {
+    if (row_to_src[r] >= 0) continue;   // wave-uniform
+    uint4* d = reinterpret_cast<uint4*>(a_out + r * K);
+    for (int64_t i = lane; i < nvec; i += 64) d[i] = make_uint4(0, 0, 0, 0);
+    for (int64_t kb = lane; kb < nkb; kb += 64) sa_out[kb * M_cap + r] = 0.0f;
   }
 }
 
@@ -172,47 +335,84 @@ hipError_t launch_permute(const int32_t* ids, int64_t T, int32_t k, int32_t E, i
   }
   const int64_t nblk = (pairs + kChunk - 1) / kChunk;
   int32_t* hist = reinterpret_cast<int32_t*>(ws);
-  hipLaunchKernelGGL(permute_hist_kernel, dim3((unsigned)nblk), dim3(256), 0, st, ids, pairs, (int)E, hist);
-  hipLaunchKernelGGL(permute_scan_kernel, dim3(1), dim3(1024), 0, st, hist, nblk, (int)E, (int)align, offsets, counts);
-  if (M_cap > 0) {
-    const int64_t g = (M_cap + 255) / 256;
-    hipLaunchKernelGGL(fill_i32_kernel, dim3((unsigned)(g < 2048 ? g : 2048)), dim3(256), 0, st, row_to_src, M_cap, -1);
-  }
-  hipLaunchKernelGGL(permute_scatter_kernel, dim3((unsigned)nblk), dim3(256), 0, st, ids, pairs, (int)E, hist,
-                     src_to_row, row_to_src, M_cap);
+  hipLaunchKernelGGL(permute_hist_kernel, dim3((unsigned)nblk), dim3(256), 0, st, ids, pairs, (int)E, nblk, hist,
+                     row_to_src, M_cap);
+  hipLaunchKernelGGL(permute_scan_kernel, dim3((unsigned)E), dim3(256), 0, st, hist, nblk, counts);
+  hipLaunchKernelGGL(permute_scatter_kernel, dim3((unsigned)nblk), dim3(256), 0, st, ids, pairs, (int)E,
+                     (int)align, nblk, hist, counts, offsets, src_to_row, row_to_src, M_cap);
   if (xq != nullptr && M_cap > 0) {
-    hipLaunchKernelGGL(permute_gather_kernel, dim3(2048), dim3(256), 0, st, offsets, (int)E, (int)k, row_to_src,
+    hipLaunchKernelGGL(permute_gather_kernel, dim3(1024), dim3(256), 0, st, offsets, (int)E, (int)k, row_to_src,
                        xq, xs, T, K, a_out, sa_out, M_cap);
   }
   return hipGetLastError();
 }
 
+hipError_t launch_permute_quantize(const int32_t* ids, int64_t T, int32_t k, int32_t E, int32_t align,
+                                   const void* x, bool bf16, int64_t K, int64_t ldx, int32_t* offsets,
+                                   int32_t* counts, int32_t* src_to_row, int32_t* row_to_src, uint8_t* a_out,
+                                   float* sa_out, int64_t M_cap, void* ws, int num_cus, hipStream_t st) {
+  hipError_t e = launch_permute(ids, T, k, E, align, nullptr, nullptr, K, offsets, counts, src_to_row,
+                                row_to_src, nullptr, nullptr, M_cap, ws, st);
+  if (e != hipSuccess || T == 0 || M_cap == 0) return e;
+  const unsigned grid = (unsigned)(num_cus > 0 ? num_cus * 8 : 2048);
+  if (bf16)
+    hipLaunchKernelGGL(permute_quantize_kernel<true>, dim3(grid), dim3(256), 0, st, offsets, (int)E, (int)k,
+                       src_to_row, row_to_src, x, ldx, T, K, a_out, sa_out, M_cap);
+  else
+    hipLaunchKernelGGL(permute_quantize_kernel<false>, dim3(grid), dim3(256), 0, st, offsets, (int)E, (int)k,
+                       src_to_row, row_to_src, x, ldx, T, K, a_out, sa_out, M_cap);
+  return hipGetLastError();
+}
+
 // ---------------------------------------------------------------------------
-// Combine: one 256-thread block per token; each thread owns 8 columns (16 B)
-// at a time and sums the routed slots in increasing j, fp32 FMA.
+// Combine: one 256-thread block per token.  A thread owns 16-byte column
+// chunks n = 8 * (256 c + tid), four chunks per pass; for each routed slot in
+// increasing j it loads all of its chunks of that row at once, then
+// accumulates them with fp32 FMA (the same order for every column).
 __global__ void __launch_bounds__(256) combine_kernel(const uint16_t* __restrict__ y, int64_t ldy,
                                                        const int32_t* __restrict__ src_to_row,
                                                        const float* __restrict__ w, int64_t T, int k,
                                                        int64_t N, uint16_t* __restrict__ out, int64_t ldo) {
+  constexpr int C = 4;
   const int64_t t = blockIdx.x;
-  for (int64_t n0 = (int64_t)threadIdx.x * 8; n0 < N; n0 += 256 * 8) {
-    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (int64_t base = 0; base < N; base += C * 2048) {
+    float acc[C][8];
+#pragma unroll
+    for (int c = 0; c < C; ++c)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[c][i] = 0.0f;
     for (int j = 0; j < k; ++j) {
       const int32_t row = src_to_row[t * k + j];
       if (row < 0) continue;
       const float wj = w[t * k + j];
-      const uint4 u = *reinterpret_cast<const uint4*>(y + (int64_t)row * ldy + n0);
-      const uint32_t q[4] = {u.x, u.y, u.z, u.w};
+      const uint16_t* yr = y + (int64_t)row * ldy;
+      uint4 u[C];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        acc[2 * i] = fmaf(wj, bf16_to_f32((uint16_t)(q[i] & 0xFFFFu)), acc[2 * i]);
-        acc[2 * i + 1] = fmaf(wj, bf16_to_f32((uint16_t)(q[i] >> 16)), acc[2 * i + 1]);
+      for (int c = 0; c < C; ++c) {
+        const int64_t n0 = base + 8 * (256 * c + threadIdx.x);
+        if (n0 < N) u[c] = *reinterpret_cast<const uint4*>(yr + n0);
+      }
+#pragma unroll
+      for (int c = 0; c < C; ++c) {
+        const uint32_t q[4] = {u[c].x, u[c].y, u[c].z, u[c].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          acc[c][2 * i] = fmaf(wj, bf16_to_f32((uint16_t)(q[i] & 0xFFFFu)), acc[c][2 * i]);
+          acc[c][2 * i + 1] = fmaf(wj, bf16_to_f32((uint16_t)(q[i] >> 16)), acc[c][2 * i + 1]);
+        }
       }
     }
-    uint32_t o[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) o[i] = (uint32_t)bf16_bits_rne(acc[2 * i]) | ((uint32_t)bf16_bits_rne(acc[2 * i + 1]) << 16);
-    *reinterpret_cast<uint4*>(out + t * ldo + n0) = make_uint4(o[0], o[1], o[2], o[3]);
+    for (int c = 0; c < C; ++c) {
+      const int64_t n0 = base + 8 * (256 * c + threadIdx.x);
+      if (n0 < N) {
+        uint32_t o[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          o[i] = (uint32_t)bf16_bits_rne(acc[c][2 * i]) | ((uint32_t)bf16_bits_rne(acc[c][2 * i + 1]) << 16);
+        *reinterpret_cast<uint4*>(out + t * ldo + n0) = make_uint4(o[0], o[1], o[2], o[3]);
+      }
+    }
   }
 }
 

@@ -11,24 +11,6 @@
 
 namespace fgg {
 
-template <bool BF16>
-__device__ inline void load8(const void* base, int64_t idx, float* f) {
-  if (BF16) {
-    const uint4 u = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(base) + idx);
-    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      f[2 * i] = bf16_to_f32((uint16_t)(w[i] & 0xFFFFu));
-      f[2 * i + 1] = bf16_to_f32((uint16_t)(w[i] >> 16));
-    }
-  } else {
-    const float4* p = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(base) + idx);
-    const float4 a = p[0], b = p[1];
-    f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
-    f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
-  }
-}
-
 // ---------------------------------------------------------------------------
 // 1 x 128 activation groups -> e4m3, scales [cols/128][rows].
 // 16 threads per group (8 elements each); a 256-thread block covers 16 groups
@@ -61,7 +43,7 @@ __global__ void __launch_bounds__(256) quant_e4m3_1x128_kernel(const void* __res
         float u[8];
         load8<BF16>(x, row * ldx + cols + col, u);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) v[i] = v[i] / (1.0f + expf(-v[i])) * u[i];
+        for (int i = 0; i < 8; ++i) v[i] = div_by_ge1(v[i], 1.0f + expf(-v[i])) * u[i];
       }
     } else {
 #pragma unroll
@@ -72,12 +54,13 @@ __global__ void __launch_bounds__(256) quant_e4m3_1x128_kernel(const void* __res
     for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
     amax = group_max<16>(amax);
     const float s = (amax == 0.0f) ? 1.0f : amax / 448.0f;
+    const float r = __builtin_amdgcn_rcpf(s);
     if (live) {
-      uint32_t lo = 0, hi = 0;
+      float y[8];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) lo |= (uint32_t)e4m3_encode(v[i] / s) << (8 * i);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) hi |= (uint32_t)e4m3_encode(v[4 + i] / s) << (8 * i);
+      for (int i = 0; i < 8; ++i) y[i] = e4m3_quotient(v[i], s, r);
+      const uint32_t lo = e4m3_pack4(y[0], y[1], y[2], y[3]);
+      const uint32_t hi = e4m3_pack4(y[4], y[5], y[6], y[7]);
       *reinterpret_cast<uint2*>(q + row * cols + col) = make_uint2(lo, hi);
       if (sub == 0) scales[kb * rows + row] = s;
     }
@@ -108,16 +91,16 @@ __global__ void __launch_bounds__(256) quant_e4m3_128x128_kernel(const void* __r
   __syncthreads();
   amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   const float s = (amax == 0.0f) ? 1.0f : amax / 448.0f;
+  const float r = __builtin_amdgcn_rcpf(s);
   uint8_t* dst = q + row * cols + col;
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
     uint32_t w[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      uint32_t word = 0;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) word |= (uint32_t)e4m3_encode(v[16 * c + 4 * j + i] / s) << (8 * i);
-      w[j] = word;
+      const float* p = v + 16 * c + 4 * j;
+      w[j] = e4m3_pack4(e4m3_quotient(p[0], s, r), e4m3_quotient(p[1], s, r), e4m3_quotient(p[2], s, r),
+                        e4m3_quotient(p[3], s, r));
     }
     *reinterpret_cast<uint4*>(dst + 16 * c) = make_uint4(w[0], w[1], w[2], w[3]);
   }

@@ -159,6 +159,27 @@ fgg_status fgg_moe_permute(const int32_t* topk_ids, int64_t T, int32_t k, int32_
                            void* stream);
 
 /*
+ * fgg_moe_permute_quantize — fgg_moe_permute with the activation quantization
+ * fused into the gather.
+ *
+ * [MegaMoE] www.mqxn.cn/news/59821 §3 fuses the token quantization into the
+ * dispatch; the rule is that of fgg_quantize_blockwise with {E4M3, F32, 1, 128}
+ * ([DeepGEMM] §5.2: s = max|x| / 448 per 1x128 group, codes = round(x / s)).
+ * x: [T][K] bf16 or fp32 token activations, row stride ldx >= K (elements),
+ * 16-byte aligned rows.  Every output (offsets, counts, src_to_row,
+ * row_to_src, a_out [M_cap][K] codes, sa_out [K/128][M_cap] scales) is
+ * bit-identical to fgg_quantize_blockwise(x) followed by fgg_moe_permute with
+ * its xq/xs; only the token-order codes are never materialised, and tokens
+ * with no routed pair are not read.  Same limits, workspace and error rules
+ * as fgg_moe_permute; x_dtype other than BF16/F32 is FGG_ERR_UNSUPPORTED.
+ */
+fgg_status fgg_moe_permute_quantize(const int32_t* topk_ids, int64_t T, int32_t k, int32_t E, int32_t align,
+                                    const void* x, fgg_dtype x_dtype, int64_t K, int64_t ldx,
+                                    int32_t* offsets, int32_t* counts, int32_t* src_to_row,
+                                    int32_t* row_to_src, void* a_out, float* sa_out, int64_t M_cap,
+                                    void* workspace, size_t ws_bytes, void* stream);
+
+/*
  * fgg_grouped_gemm_scaled — one launch for all groups (experts).
  *
  * The per-group formula of [Infra] Q "量化矩阵乘的维度和流程" with both

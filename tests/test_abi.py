@@ -25,7 +25,8 @@ def _declared():
 
 def test_header_declares_the_boundary():
     names = _declared()
-    for n in ["fgg_quantize_blockwise", "fgg_moe_permute", "fgg_moe_permute_workspace", "fgg_grouped_gemm_scaled",
+    for n in ["fgg_quantize_blockwise", "fgg_moe_permute", "fgg_moe_permute_workspace", "fgg_moe_permute_quantize",
+              "fgg_grouped_gemm_scaled",
               "fgg_scaled_gemm", "fgg_scaled_gemm_workspace", "fgg_moe_combine", "fgg_status_string",
               "fgg_last_hip_error", "fgg_set_num_cus"]:
         assert n in names
@@ -106,5 +107,12 @@ def test_gemm_and_permute_reject_bad_arguments_on_host():
     assert lib.fgg_moe_permute(g, 10, 2, 4, 128, None, None, 0, g, g, g, g, None, None, 100, None, 0, None) == 1
     n = ctypes.c_size_t(0)
     assert lib.fgg_moe_permute_workspace(10, 2, 4, ctypes.byref(n)) == 0 and n.value > 0
+    # fused permute + quantize: bad dtype, K not a multiple of 128, short row stride, missing workspace
+    Q = lib.fgg_moe_permute_quantize
+    assert Q(g, 10, 2, 4, 128, g, fgg.FGG_E4M3, 256, 256, g, g, g, g, g, g, 100, g, 1 << 20, None) == 2
+    assert Q(g, 10, 2, 4, 128, g, fgg.FGG_BF16, 200, 256, g, g, g, g, g, g, 100, g, 1 << 20, None) == 2
+    assert Q(g, 10, 2, 4, 128, g, fgg.FGG_BF16, 256, 128, g, g, g, g, g, g, 100, g, 1 << 20, None) == 1
+    assert Q(g, 10, 2, 4, 128, g, fgg.FGG_BF16, 256, 256, g, g, g, g, g, g, 100, None, 0, None) == 1
+    assert Q(g, 10, 2, 2000, 128, g, fgg.FGG_BF16, 256, 256, g, g, g, g, g, g, 100, g, 1 << 20, None) == 1
     # combine: N not a multiple of 8
     assert lib.fgg_moe_combine(g, 16, g, g, 4, 2, 12, g, 16, None) == 2

@@ -115,3 +115,80 @@ def test_combine_unit_weight_single_slot_is_exact_gather():
     y = synth.to_bf16_values(synth.normal(g, (int(ref_perm["offsets"][-1]), N)))
     out = fgg.moe_combine(cuda(y, torch.bfloat16), cuda(ref_perm["src_to_row"]), cuda(np.ones((T, 1), np.float32)))
     assert np.array_equal(to_np(out), y[ref_perm["src_to_row"]])
+
+
+# ------------------------------------------------ fused quantize + permute
+
+def _x_input(seed, T, K, dtype):
+    x = synth.normal(synth.rng(seed), (T, K)) * np.float32(2.0)
+    if T > 3:
+        x[1, :128] = 0.0                  # an all-zero group
+        x[2, 5] = 1e30                    # one huge value sets its group's scale
+        x[3, 7] = -0.0                    # signed zero keeps its sign code
+        x[3, 130:140] = 1e-30             # tiny values beside normal ones
+    if dtype == torch.bfloat16:
+        x = synth.to_bf16_values(x)
+    return x
+
+
+@pytest.mark.parametrize("T,k,E,K,dtype", [(64, 2, 4, 256, torch.bfloat16), (300, 8, 32, 640, torch.float32),
+                                           (1000, 6, 17, 1152, torch.bfloat16), (5000, 4, 256, 128, torch.float32),
+                                           (777, 3, 5, 2560, torch.bfloat16)])
+def test_permute_quantize_matches_oracle_and_unfused(T, k, E, K, dtype):
+    g = synth.rng(T + 3 * k + E + K)
+    ids = g.integers(-3, E + 3, size=(T, k)).astype(np.int32)
+    x = _x_input(T + K, T, K, dtype)
+    xt = cuda(x, dtype)
+    out = fgg.moe_permute_outputs(T, k, E, 128, K)
+    out["a"].fill_(0xAB)
+    out["sa"].fill_(-7.0)
+    got = fgg.moe_permute(cuda(ids), E, 128, x=xt, out=out)
+    ref = oracle.moe_permute(ids, E, 128)
+    mt = int(ref["offsets"][-1])
+    aq_r, sa_r = oracle.quantize_e4m3_blocks(x, 1, 128)
+    a_ref, s_ref = oracle.gather_permuted(ref["row_to_src"], mt, k, aq_r, sa_r)
+    assert np.array_equal(to_np(got["offsets"]), ref["offsets"])
+    assert np.array_equal(to_np(got["src_to_row"]), ref["src_to_row"])
+    assert np.array_equal(to_np(got["row_to_src"]), ref["row_to_src"][:got["m_cap"]])
+    a, sa = to_np(got["a"]), to_np(got["sa"])
+    assert np.array_equal(a[:mt], a_ref)
+    assert np.array_equal(sa[:, :mt], s_ref.T)
+    assert np.all(a[mt:] == 0xAB) and np.all(sa[:, mt:] == -7.0)       # rows >= M_total untouched
+    # the unfused pair of calls gives the same bytes
+    xq, xs = fgg.quantize_blockwise(xt, fgg.Q_E4M3_1x128)
+    unf = fgg.moe_permute(cuda(ids), E, 128, xq=xq, xs=xs)
+    assert torch.equal(unf["a"][:mt], got["a"][:mt]) and torch.equal(unf["sa"][:, :mt], got["sa"][:, :mt])
+
+
+def test_permute_quantize_moe_prefill_full_size():
+    r = synth.moe_prefill_routing()
+    x = synth.to_bf16_values(synth.moe_prefill_x())
+    T, K = x.shape
+    got = fgg.moe_permute(cuda(r["topk_ids"]), 32, 128, x=cuda(x, torch.bfloat16))
+    ref = oracle.moe_permute(r["topk_ids"], 32, 128)
+    mt = int(ref["offsets"][-1])
+    assert mt == 10112 and np.array_equal(to_np(got["offsets"]), ref["offsets"])
+    # sampled rows: each row's codes/scales against the oracle's quantization of its token
+    rows = np.array([0, 1, 127, 128, 2323, 2400, 5000, 9000, 10111])
+    r2s = ref["row_to_src"][rows]
+    a, sa = to_np(got["a"]), to_np(got["sa"])
+    for row, p in zip(rows, r2s):
+        if p < 0:
+            assert np.all(a[row] == 0) and np.all(sa[:, row] == 0)
+        else:
+            qr, sr = oracle.quantize_e4m3_blocks(x[p // 8][None], 1, 128)
+            assert np.array_equal(a[row], qr[0]) and np.array_equal(sa[:, row], sr[0])
+
+
+def test_permute_quantize_small_m_cap_and_zero_tokens():
+    ids = np.zeros((64, 2), np.int32)                    # needs 128 rows
+    x = cuda(_x_input(5, 64, 128, torch.float32))
+    out = fgg.moe_permute_outputs(64, 2, 2, 128, 128, m_cap=100)
+    got = fgg.moe_permute(cuda(ids), 2, 128, x=x, out=out)
+    assert to_np(got["offsets"]).tolist() == [0, 128, 128]
+    assert np.array_equal(to_np(got["row_to_src"]), np.arange(100))
+    aq_r, sa_r = oracle.quantize_e4m3_blocks(to_np(x), 1, 128)
+    a = to_np(got["a"])
+    assert np.array_equal(a[:100], aq_r[np.arange(100) // 2])
+    got0 = fgg.moe_permute(cuda(np.zeros((0, 4), np.int32)), 3, 128, x=torch.zeros((0, 256), device="cuda"))
+    assert to_np(got0["offsets"]).tolist() == [0, 0, 0, 0]
