@@ -249,23 +249,46 @@ gemm_fp8_contig_kernel(int G, int64_t M, int64_t N, int64_t K, const uint8_t* __
         f.b[j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
       }
     };
-    // 16 MFMAs, each promoted with 4 FMAs.  The promotion of MFMA t is issued after
-    // MFMA t+2 (a 2-deep pipeline through three result registers), so the matrix
-    // core never waits for the vector ALU and the FMAs never wait for a result that
-    // is still in flight.  The LDS reads of the next K block's fragments go out in
-    // the first half of the MFMA run (two per MFMA) so that they have landed by the
-    // wait at the top of the next step.  The sched_group_barrier sequence pins this.
-    auto mma = [&](const Frags& f, float sb) {
+    // One K block: 16 MFMAs, each promoted with 4 FMAs, interleaved with the LDS
+    // reads of the next K block's fragments (stage NST).  Program order is pinned
+    // group by group with full scheduling barriers: MFMA t, then two of the 20
+    // fragment / scale reads (during MFMAs 0..9), then the promotion of MFMA t-2.
+    // The promotion therefore trails its MFMA by two MFMA issues (three result
+    // registers in rotation), so the matrix core never waits for the vector ALU
+    // and no FMA waits for a result still in flight.
+    auto mma_and_read = [&](const Frags& f, float sb, auto nst_tag, Frags& nxt) {
+      constexpr int NST = decltype(nst_tag)::value;
       float sab[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) sab[i] = f.s[i] * sb;
       constexpr int T = 4 * kNFrag;
       v4f p[3];
+      uint4 rd[20];
+      auto read = [&](int r) {
+        // reads 0..7: A fragments (lo, hi); 8..11: activation scales; 12..19: B fragments
+        if (r < 8) {
+          const int i = r >> 1;
+          const uint32_t off = ((r & 1) ? ra_hi : ra_lo) + NST * kABytes + i * 16 * BK;
+          rd[r] = *reinterpret_cast<const uint4*>(smem + off);
+        } else if (r < 12) {
+          const int i = r - 8;
+          nxt.s[i] = *reinterpret_cast<const float*>(smem + rs + NST * kSBytes + i * 16 * 4);
+        } else {
+          const int j = (r - 12) >> 1;
+          const uint32_t off = ((r & 1) ? rb_hi : rb_lo) + NST * kBBytes + j * 16 * BK;
+          rd[r] = *reinterpret_cast<const uint4*>(smem + off);
+        }
+      };
 #pragma unroll
       for (int t = 0; t < T + 2; ++t) {
         if (t < T) {
           p[t % 3] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
               f.b[t % kNFrag], f.a[t / kNFrag], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (t < 10) {
+          read(2 * t);
+          read(2 * t + 1);
         }
         if (t >= 2) {
           const int u = t - 2;
@@ -277,16 +300,18 @@ gemm_fp8_contig_kernel(int G, int64_t M, int64_t N, int64_t K, const uint8_t* __
           c[2] = fmaf(r[2], sc, c[2]);
           c[3] = fmaf(r[3], sc, c[3]);
         }
+        __builtin_amdgcn_sched_barrier(0);
       }
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);     // MFMA 0, 1
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);     // 2 LDS reads
 #pragma unroll
-      for (int t = 2; t < T; ++t) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA t
-        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);   // promotion of MFMA t-2
-        if (t < 10) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // 2 LDS reads
+      for (int i = 0; i < 4; ++i) {
+        const uint4 lo = rd[2 * i], hi = rd[2 * i + 1];
+        nxt.a[i] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
       }
-      __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);     // promotion of the last two
+#pragma unroll
+      for (int j = 0; j < kNFrag; ++j) {
+        const uint4 lo = rd[12 + 2 * j], hi = rd[13 + 2 * j];
+        nxt.b[j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      }
     };
 
     // Pipeline.  Stage j lives in LDS buffer j % 3 and is read into registers during
@@ -306,10 +331,9 @@ gemm_fp8_contig_kernel(int G, int64_t M, int64_t N, int64_t K, const uint8_t* __
       else wait_vmcnt<0>();
       block_barrier();
       if (kb + 3 < nkb) issue(kb + 3, ST);
-      // unconditional (the last step's reads are unused but in bounds): keeping the reads
-      // and the MFMAs in one basic block lets the scheduler interleave them
-      load_frags(std::integral_constant<int, (ST + 1) % kStages>{}, nxt);
-      mma(cur, sb_cur);
+      // unconditional (the last step's reads are unused but in bounds): the reads and
+      // the MFMAs stay in one basic block, interleaved in a fixed order
+      mma_and_read(cur, sb_cur, std::integral_constant<int, (ST + 1) % kStages>{}, nxt);
       sb_cur = sbl_w[kb + 1 < nkb ? kb + 1 : kb];      // read now, waited at the next step's top
     };
 
