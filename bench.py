@@ -201,7 +201,7 @@ def bench_w4a4(fgg, synth, torch, iters=30):
     lu = synth.normal_cuda(61_003, (r, N), 0.01).to(torch.bfloat16)
     bias = synth.normal_cuda(61_004, (N,), 0.1).to(torch.bfloat16)
     d = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
-    ws = torch.empty(M * r * 2, dtype=torch.uint8, device="cuda")
+    ws = torch.empty(fgg.scaled_gemm_workspace_bytes(M, N, K, "w4a4", rank=r), dtype=torch.uint8, device="cuda")
     ms = time_calls(lambda i: fgg.scaled_gemm(xq, xs, wq, wsc, qdesc="w4a4", x_bf16=x, l_down=ld, l_up=lu,
                                               bias=bias, out=d, workspace=ws), iters, 5)
     flops = 2.0 * M * N * K + 2.0 * M * r * (K + N)

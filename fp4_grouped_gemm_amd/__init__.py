@@ -254,6 +254,16 @@ def grouped_gemm_scaled(a, a_scales, b, b_scales, offsets=None, masked_m=None,
     return out
 
 
+def scaled_gemm_workspace_bytes(M: int, N: int, K: int, qdesc: str = "fp8", rank: int = 0) -> int:
+    """Workspace bytes scaled_gemm needs (fgg_scaled_gemm_workspace)."""
+    aq, bq = (Q_E4M3_1x128, Q_E4M3_128x128) if qdesc == "fp8" else (Q_E2M1_1x16, Q_E2M1_1x16)
+    epi = Epilogue(None, None, None, int(rank), None)
+    n = ctypes.c_size_t(0)
+    _check("fgg_scaled_gemm_workspace", load_library().fgg_scaled_gemm_workspace(
+        M, N, K, _q(aq), _q(bq), ctypes.byref(epi), ctypes.byref(n)))
+    return n.value
+
+
 def scaled_gemm(a, a_scales, b, b_scales, qdesc="fp8", x_bf16=None, l_down=None, l_up=None, bias=None,
                 out=None, workspace=None):
     """Dense case.  qdesc "fp8": a [M, K] e4m3 with [K/128, M] scales, b [N, K]

@@ -220,7 +220,7 @@ fgg_status fgg_scaled_gemm_workspace(int64_t M, int64_t N, int64_t K, fgg_qdesc 
   if (!bytes || M < 0) return FGG_ERR_INVALID_VALUE;
   *bytes = 0;
   if (same_q(aq, FGG_E2M1X2, FGG_F32, 1, 16) && same_q(bq, FGG_E2M1X2, FGG_F32, 1, 16) && epi && epi->rank > 0)
-    *bytes = fgg::w4a4_workspace_bytes(M, epi->rank);
+    *bytes = fgg::w4a4_workspace_bytes(M, K, epi->rank);
   return FGG_OK;
 }
 
@@ -253,7 +253,7 @@ fgg_status fgg_scaled_gemm(int64_t M, int64_t N, int64_t K, const void* a, const
       if (!epi->x_bf16 || !epi->l_down || !epi->l_up) return FGG_ERR_INVALID_VALUE;
       if (!aligned(epi->x_bf16, 16) || !aligned(epi->l_down, 2) || !aligned(epi->l_up, 2))
         return FGG_ERR_INVALID_VALUE;
-      if (!workspace || ws_bytes < fgg::w4a4_workspace_bytes(M, rank) || !aligned(workspace, 16))
+      if (!workspace || ws_bytes < fgg::w4a4_workspace_bytes(M, K, rank) || !aligned(workspace, 16))
         return FGG_ERR_INVALID_VALUE;
     }
     const void* bias = epi ? epi->bias : nullptr;

@@ -9,9 +9,9 @@
 // M·N·K/16 FMAs (more than the matrix work).  So each operand tile is
 // dequantized once on its way into LDS, x·s rounded to fp16, and contracted
 // with v_mfma_f32_16x16x32_f16 in fp32.  The low-rank branch is a separate
-// small kernel for T = X·L_down (fp32 accumulate, stored bf16 in the
-// workspace) and one extra bf16 MFMA step T·L_up per output tile, before the
-// bias is added in the epilogue.
+// small bf16-MFMA kernel for T = X·L_down (fp32 accumulate, stored bf16 in
+// the workspace, with L_down transposed there first) and one extra bf16 MFMA
+// step T·L_up per output tile, before the bias is added in the epilogue.
 //
 // Tile: 128 x 128 per 256-thread workgroup (4 waves of 64 x 64); one 128-wide
 // K block per LDS stage (2 x 128 x 128 fp16 = 64 KB); 16-byte chunks of each
@@ -59,31 +59,72 @@ __device__ inline void dequant32(uint4 packed, float s0, float s1, uint4* out4) 
 __device__ inline int swz16(int row) { return row & 15; }
 }  // namespace
 
-// T[m][r] = Σ_k X[m][k] · L_down[k][r] in fp32, stored bf16.  8 rows x 32 ranks per block.
+// L_down [K][32] -> LdT [32][K] (bf16), so that both operands of T = X·L_down
+// are K-contiguous.
+__global__ void __launch_bounds__(256) w4a4_ld_transpose_kernel(const uint16_t* __restrict__ Ld, int64_t K,
+                                                                uint16_t* __restrict__ LdT) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;   // over K*32, rank fastest (coalesced reads)
+  if (i >= K * 32) return;
+  const int64_t k = i >> 5, r = i & 31;
+  LdT[r * K + k] = Ld[i];
+}
+
+// T[m][r] = Σ_k X[m][k] · L_down[k][r] (rank 32), fp32 accumulate, stored bf16.
+// One 256-thread block per 16 rows; wave w sums K range [w·K/4, (w+1)·K/4) with
+// v_mfma_f32_16x16x32_bf16 (first operand: 16 ranks of LdT, second: the 16 X
+// rows; lane (l, q) holds K elements [8q, 8q+8) of row l of each), two rank
+// tiles per wave; the four partial sums are added in wave order through LDS.
 __global__ void __launch_bounds__(256) w4a4_lowrank_down_kernel(const uint16_t* __restrict__ X, int64_t M, int64_t K,
-                                                                 const uint16_t* __restrict__ Ld, int rank,
+                                                                 const uint16_t* __restrict__ LdT,
                                                                  uint16_t* __restrict__ T) {
-  __shared__ float xs[8][256];
-  __shared__ float ls[256][33];
-  const int r = threadIdx.x & 31, i = threadIdx.x >> 5;
-  const int64_t m = (int64_t)blockIdx.x * 8 + i;
-  float acc = 0.0f;
-  for (int64_t k0 = 0; k0 < K; k0 += 256) {
-    for (int idx = threadIdx.x; idx < 8 * 256; idx += 256) {
-      const int ii = idx >> 8, kk = idx & 255;
-      const int64_t mm = (int64_t)blockIdx.x * 8 + ii;
-      xs[ii][kk] = (mm < M && k0 + kk < K) ? bf16_to_f32(X[mm * K + k0 + kk]) : 0.0f;
+  __shared__ v4f part[4][2][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int l16 = lane & 15, q = lane >> 4;
+  const int64_t m0 = (int64_t)blockIdx.x * 16;
+  int64_t mrow = m0 + l16;
+  if (mrow >= M) mrow = M - 1;               // rows past the end read a valid row; never stored
+  const int64_t kq = K / 4;                  // K % 128 == 0, so kq % 32 == 0
+  const int64_t k_begin = wave * kq, k_end = k_begin + kq;
+  const uint16_t* xr = X + mrow * K + 8 * q;
+  const uint16_t* l0 = LdT + (int64_t)l16 * K + 8 * q;
+  const uint16_t* l1 = LdT + (int64_t)(16 + l16) * K + 8 * q;
+  v4f acc0 = v4f{0.f, 0.f, 0.f, 0.f}, acc1 = v4f{0.f, 0.f, 0.f, 0.f};
+  for (int64_t k = k_begin; k < k_end; k += 128) {
+    uint4 xa[4], la[4], lb[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (k + 32 * u >= k_end) break;       // wave-uniform: the range is a multiple of 32
+      xa[u] = *reinterpret_cast<const uint4*>(xr + k + 32 * u);
+      la[u] = *reinterpret_cast<const uint4*>(l0 + k + 32 * u);
+      lb[u] = *reinterpret_cast<const uint4*>(l1 + k + 32 * u);
     }
-    for (int idx = threadIdx.x; idx < 256 * 32; idx += 256) {
-      const int kk = idx >> 5, rr = idx & 31;
-      ls[kk][rr] = (k0 + kk < K && rr < rank) ? bf16_to_f32(Ld[(k0 + kk) * rank + rr]) : 0.0f;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (k + 32 * u >= k_end) break;
+      const v8bf xv = __builtin_bit_cast(v8bf, xa[u]);
+      acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, la[u]), xv, acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, lb[u]), xv, acc1, 0, 0, 0);
     }
-    __syncthreads();
-#pragma unroll 8
-    for (int kk = 0; kk < 256; ++kk) acc = fmaf(xs[i][kk], ls[kk][r], acc);
-    __syncthreads();
   }
-  if (m < M && r < rank) T[m * rank + r] = bf16_bits_rne(acc);
+  part[wave][0][lane] = acc0;
+  part[wave][1][lane] = acc1;
+  __syncthreads();
+  if (wave != 0) return;
+  // lane (l16, q) holds ranks 4q..4q+3 (tile 0) and 16+4q.. (tile 1) of row m0 + l16
+  v4f s0 = part[0][0][lane], s1 = part[0][1][lane];
+#pragma unroll
+  for (int w = 1; w < 4; ++w) {
+    const v4f a = part[w][0][lane], b = part[w][1][lane];
+    s0[0] += a[0]; s0[1] += a[1]; s0[2] += a[2]; s0[3] += a[3];
+    s1[0] += b[0]; s1[1] += b[1]; s1[2] += b[2]; s1[3] += b[3];
+  }
+  const int64_t m = m0 + l16;
+  if (m >= M) return;
+  uint16_t* t = T + m * 32 + 4 * q;
+  *reinterpret_cast<uint2*>(t) = make_uint2((uint32_t)bf16_bits_rne(s0[0]) | ((uint32_t)bf16_bits_rne(s0[1]) << 16),
+                                            (uint32_t)bf16_bits_rne(s0[2]) | ((uint32_t)bf16_bits_rne(s0[3]) << 16));
+  *reinterpret_cast<uint2*>(t + 16) = make_uint2((uint32_t)bf16_bits_rne(s1[0]) | ((uint32_t)bf16_bits_rne(s1[1]) << 16),
+                                                 (uint32_t)bf16_bits_rne(s1[2]) | ((uint32_t)bf16_bits_rne(s1[3]) << 16));
 }
 
 __global__ void __launch_bounds__(256, 1)
@@ -208,7 +249,11 @@ w4a4_gemm_kernel(int64_t M, int64_t N, int64_t K, const uint8_t* __restrict__ A,
   }
 }
 
-size_t w4a4_workspace_bytes(int64_t M, int32_t rank) { return (size_t)(M * rank * 2); }
+// workspace: T [M][32] bf16, then LdT [32][K] bf16 (16-byte aligned)
+size_t w4a4_workspace_bytes(int64_t M, int64_t K, int32_t rank) {
+  if (rank == 0) return 0;
+  return (size_t)(((M * 32 * 2 + 15) / 16) * 16 + 32 * K * 2);
+}
 
 hipError_t launch_w4a4(int64_t M, int64_t N, int64_t K, const uint8_t* a, const float* sa,
                        const uint8_t* b, const float* sb, const uint16_t* x_bf16,
@@ -217,8 +262,11 @@ hipError_t launch_w4a4(int64_t M, int64_t N, int64_t K, const uint8_t* a, const 
   if (M == 0 || N == 0) return hipSuccess;
   uint16_t* T = reinterpret_cast<uint16_t*>(ws);
   if (rank > 0) {
-    hipLaunchKernelGGL(w4a4_lowrank_down_kernel, dim3((unsigned)((M + 7) / 8)), dim3(256), 0, st, x_bf16, M, K,
-                       l_down, (int)rank, T);
+    uint16_t* LdT = reinterpret_cast<uint16_t*>(reinterpret_cast<uint8_t*>(ws) + ((M * 32 * 2 + 15) / 16) * 16);
+    hipLaunchKernelGGL(w4a4_ld_transpose_kernel, dim3((unsigned)((K * 32 + 255) / 256)), dim3(256), 0, st, l_down, K,
+                       LdT);
+    hipLaunchKernelGGL(w4a4_lowrank_down_kernel, dim3((unsigned)((M + 15) / 16)), dim3(256), 0, st, x_bf16, M, K,
+                       LdT, T);
   }
   const int64_t tiles = (M / BM) * (N / BN);
   hipLaunchKernelGGL(w4a4_gemm_kernel, dim3((unsigned)tiles), dim3(256), 0, st, M, N, K, a, sa, b, sb,

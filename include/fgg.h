@@ -223,10 +223,11 @@ fgg_status fgg_grouped_gemm_scaled(fgg_layout layout, int32_t G, int64_t M, int6
  *   D = bf16( Σ_g16 sA[m,g]·sB[n,g]·Σ_{k in g} A[m][k]·B[n][k]
  *             + (x_bf16 · l_down) · l_up + bias )
  *   The operands are dequantized on chip to fp16 (x·s rounded once) and
- *   contracted with fp16 MFMA in fp32; the rank-`rank` intermediate is
- *   rounded to fp16.  Requires M % 128 == 0, K % 128 == 0, N % 128 == 0.
+ *   contracted with fp16 MFMA in fp32; the rank-32 intermediate
+ *   x_bf16 · l_down is accumulated in fp32 (bf16 MFMA) and rounded to bf16.
+ *   Requires M % 128 == 0, K % 128 == 0, N % 128 == 0, rank in {0, 32}.
  *   With a low-rank branch, workspace must hold fgg_scaled_gemm_workspace()
- *   bytes (the [M][rank] intermediate).
+ *   bytes (the [M][32] intermediate and a [32][K] transposed copy of l_down).
  */
 fgg_status fgg_scaled_gemm_workspace(int64_t M, int64_t N, int64_t K, fgg_qdesc aq, fgg_qdesc bq,
                                      const fgg_epilogue* epi, size_t* bytes);

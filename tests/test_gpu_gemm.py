@@ -363,3 +363,25 @@ def test_w4a4_full_size_sampled():
     wl = synth.w4a4()
     y, ref = _w4a4_run(wl, rows=np.array([0, 1, 63, 64, 1000, 2048, 4000, 4095]))
     tol_check(y, ref, what="w4a4 4096x3072x3072 sampled rows")
+
+
+@pytest.mark.parametrize("M,N,K", [(128, 256, 384), (256, 128, 3072)])
+def test_w4a4_lowrank_branch_alone(M, N, K):
+    # all-zero FP4 codes: the block-scaled product vanishes and the output is the
+    # low-rank term plus bias alone, so a mistake there cannot hide under the
+    # tolerance of the (much larger) main product; K = 384 gives each of the four
+    # K-split waves a range that is not a multiple of 128
+    wl = synth.w4a4(seed=91, M=M, N=N, K=K)
+    ld = wl["l_down"] * np.float32(20.0)           # make the rank term O(1)
+    zq = torch.zeros((M, K // 2), dtype=torch.uint8, device="cuda")
+    zs = torch.ones((M, K // 16), dtype=torch.float32, device="cuda")
+    wq = torch.zeros((N, K // 2), dtype=torch.uint8, device="cuda")
+    ws = torch.ones((N, K // 16), dtype=torch.float32, device="cuda")
+    y = fgg.scaled_gemm(zq, zs, wq, ws, qdesc="w4a4", x_bf16=cuda(wl["x"], torch.bfloat16),
+                        l_down=cuda(synth.to_bf16_values(ld), torch.bfloat16),
+                        l_up=cuda(wl["l_up"], torch.bfloat16), bias=cuda(wl["bias"], torch.bfloat16))
+    ref = oracle.round_bf16(oracle.w4a4_lowrank_gemm(
+        np.zeros((M, K), np.uint8), np.ones((M, K // 16), np.float32), np.zeros((N, K), np.uint8),
+        np.ones((N, K // 16), np.float32), wl["x"], synth.to_bf16_values(ld), wl["l_up"], wl["bias"]))
+    assert np.abs(ref).max() > 0.1                  # the branch is really exercised
+    tol_check(to_np(y), ref, what="w4a4 low-rank branch")
