@@ -1,5 +1,8 @@
-// Block-scaled FP8 x FP8 grouped GEMM, contiguous (prefill) layout; the dense
-// GEMM is the one-group case.
+// Block-scaled FP8 x FP8 grouped GEMM, contiguous (prefill) layout, and the
+// dense (one-group) GEMM.  Two kernels: gemm_fp8_contig_kernel (128 x 256 tiles,
+// every layout) and gemm_fp8_dense_kernel (256 x 256 tiles, one group starting
+// at row 0); they compute each output with the same operations in the same
+// order, so the dense call equals the grouped call with one group bit for bit.
 //
 //   D[r][n] = bf16( Σ_kb sA[kb][r] · sB[g][n/128][kb] · Σ_{k in kb} A[r][k] · B[g][n][k] )
 //
@@ -17,7 +20,7 @@
 //    are four consecutive columns of one row: one sA per lane per 16-row
 //    subtile, one sB per wave (a wave's 64 columns lie in one 128-column scale
 //    block), and 8-byte bf16 stores.
-//  * workgroup tile 128 x 256: 8 waves of 64 x 64 (4 x 4 MFMA subtiles, 64 fp32
+//  * grouped kernel: workgroup tile 128 x 256: 8 waves of 64 x 64 (4 x 4 MFMA subtiles, 64 fp32
 //    accumulators per lane), two waves per SIMD so that one wave's MFMAs
 //    overlap the other's promotion FMAs, LDS reads and barrier waits; one
 //    workgroup per CU.
@@ -389,12 +392,227 @@ gemm_fp8_contig_kernel(int G, int64_t M, int64_t N, int64_t K, const uint8_t* __
   }
 }
 
+// ---------------------------------------------------------------------------
+// Dense (one-group) kernel with 256 x 256 tiles.  Eight waves of 128 x 64
+// outputs (8 x 4 MFMA subtiles, 128 fp32 accumulators per lane), two per SIMD:
+// a wave's operand fragments are reused by 4 (A) and 8 (B) MFMAs, so the
+// LDS-to-register traffic is 768 bytes per MFMA instead of 1 KB with 64 x 64
+// wave tiles; on gfx950 that traffic, not the matrix core, bounds the K loop
+// (moving data into VGPRs and MFMA issue largely serialize on a SIMD).  Two LDS
+// stages of 65 KB (A, B, activation scales), the DMA of K block kb+1 issued at
+// the top of step kb.  The grouped layout keeps the 128 x 256 kernel above:
+// expert segments are multiples of 128 rows, and with the ragged segment
+// lengths of MoE routing, 256-row tiles leave many half-empty tiles.
+namespace dense {
+constexpr int BM = 256, BN = 256, BK = 128;
+constexpr int kWaves = 8, kThreads = 64 * kWaves;
+constexpr int kABytes = BM * BK, kBBytes = BN * BK, kSBytes = BM * 4;
+constexpr int kStageBytes = kABytes + kBBytes + kSBytes;     // 66560
+constexpr int kMaxKb = 128;                                  // K <= 16384
+constexpr int kSBOff = 2 * kStageBytes;                      // weight scales [2][kMaxKb]
+constexpr int kLdsBytes = kSBOff + 2 * kMaxKb * 4;
+constexpr int kADma = kABytes / 1024 / kWaves;               // 4
+constexpr int kBDma = kBBytes / 1024 / kWaves;               // 4
+constexpr int kSM = 8;
+}  // namespace dense
+
+__global__ void __launch_bounds__(dense::kThreads, 1)
+gemm_fp8_dense_kernel(int64_t M, int64_t N, int64_t K, const uint8_t* __restrict__ A,
+                      const float* __restrict__ SA, const uint8_t* __restrict__ B,
+                      const float* __restrict__ SB, uint16_t* __restrict__ D, int64_t ldd) {
+  constexpr int BM = dense::BM, BN = dense::BN, BK = dense::BK, kThreads = dense::kThreads;
+  constexpr int kABytes = dense::kABytes, kBBytes = dense::kBBytes, kStageBytes = dense::kStageBytes;
+  constexpr int kMaxKb = dense::kMaxKb, kSBOff = dense::kSBOff;
+  constexpr int kADma = dense::kADma, kBDma = dense::kBDma, kSM = dense::kSM;
+  __shared__ __align__(16) uint8_t smem[dense::kLdsBytes];
+  const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave & 1, wn = wave >> 1;        // 2 x 4 waves: 128 rows x 64 columns each
+  const int l16 = lane & 15, q = lane >> 4;
+  const int nkb = (int)(K / BK);
+  const int64_t nblk = N / 128;
+  const int64_t m_tiles = (M + BM - 1) / BM, n_tiles = (N + BN - 1) / BN;
+
+  const int lrow = lane >> 3;
+  const int lchunk = (lane & 7) ^ lrow;
+  // Loop-invariant LDS read offsets (stage 0) of this lane's fragments: row tile i
+  // is 16 rows (2048 bytes) further, column tile j likewise.
+  const int arow = wm * 128 + l16, brow = wn * 64 + l16;
+  const uint32_t ra_lo = arow * BK + (((2 * q) ^ swz(arow)) << 4);
+  const uint32_t ra_hi = arow * BK + (((2 * q + 1) ^ swz(arow)) << 4);
+  const uint32_t rb_lo = kABytes + brow * BK + (((2 * q) ^ swz(brow)) << 4);
+  const uint32_t rb_hi = kABytes + brow * BK + (((2 * q + 1) ^ swz(brow)) << 4);
+  const uint32_t rs = kABytes + kBBytes + arow * 4;
+
+  const int wg_per_xcd = (int)(gridDim.x / kXcds);
+  const int xcd = (int)(blockIdx.x % kXcds), slot = (int)(blockIdx.x / kXcds);
+  const int sn_tiles = wg_per_xcd / kSM > 0 ? wg_per_xcd / kSM : 1;
+  const int64_t st_m = (m_tiles + kSM - 1) / kSM, st_n = (n_tiles + sn_tiles - 1) / sn_tiles;
+  const int64_t num_st = st_m * st_n;
+  for (int64_t st = xcd; st < num_st; st += kXcds) {
+    if (slot >= kSM * sn_tiles) break;
+    const int64_t mt = (st / st_n) * kSM + slot % kSM;
+    const int64_t nt = (st % st_n) * sn_tiles + slot / kSM;
+    if (mt >= m_tiles || nt >= n_tiles) continue;
+    const int64_t m0 = mt * BM, n0 = nt * BN;
+    const int64_t rows_here = (M - m0) < BM ? (M - m0) : BM;               // >= 1
+    const int64_t cols_here = (N - n0) < BN ? (N - n0) : BN;               // 128 or 256
+    const bool wave_live = (wm * 128 < rows_here) && (wn * 64 < cols_here);
+    const uint8_t* Atile = A + m0 * K;
+    const uint8_t* Btile = B + n0 * K;
+
+    uint32_t offA[kADma], offB[kBDma];
+#pragma unroll
+    for (int i = 0; i < kADma; ++i) {
+      const int grp8 = wave * kADma + i;
+      int row = grp8 * 8 + lrow;
+      const int c = lchunk ^ (grp8 & 1);
+      if (row >= rows_here) row = (int)rows_here - 1;
+      offA[i] = (uint32_t)(row * K + c * 16);
+    }
+#pragma unroll
+    for (int i = 0; i < kBDma; ++i) {
+      const int grp8 = wave * kBDma + i;
+      int row = grp8 * 8 + lrow;
+      const int c = lchunk ^ (grp8 & 1);
+      if (row >= cols_here) row = (int)cols_here - 1;
+      offB[i] = (uint32_t)(row * K + c * 16);
+    }
+    int srow = wave * 32 + (lane & 31);
+    if (srow >= rows_here) srow = (int)rows_here - 1;
+    const uint32_t offS = (uint32_t)(srow * 4);
+
+    auto issue = [&](int kb, int stage) {
+      const uint8_t* a_src = Atile + (int64_t)kb * BK;
+      const uint8_t* b_src = Btile + (int64_t)kb * BK;
+      const uint32_t base = lds_base + stage * kStageBytes;
+#pragma unroll
+      for (int i = 0; i < kADma; ++i) dma16(a_src, offA[i], base + (wave * kADma + i) * 1024);
+#pragma unroll
+      for (int i = 0; i < kBDma; ++i) dma16(b_src, offB[i], base + kABytes + (wave * kBDma + i) * 1024);
+      const float* s_src = SA + (int64_t)kb * M + m0;
+      if (lane < 32) dma4(s_src, offS, base + kABytes + kBBytes + wave * 128);
+    };
+
+    v4f acc[8][4];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    // One K block from LDS stage ST: B fragments first, then the A fragments
+    // streamed one row tile ahead; program order pinned group by group: MFMA t,
+    // then (at t % 4 == 0) the reads of A row tile t/4 + 1, then the promotion
+    // of MFMA t-2 (three result registers in rotation).
+    const float* sbl_w = reinterpret_cast<const float*>(smem + kSBOff) + ((wn * 64) / 128) * kMaxKb;
+    auto compute = [&](auto st_tag, int kb) {
+      constexpr int ST = decltype(st_tag)::value;
+      const uint8_t* sb = smem + ST * kStageBytes;
+      v8i bf[4], af[2];
+      float sab[8];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint4 lo = *reinterpret_cast<const uint4*>(sb + rb_lo + j * 16 * BK);
+        const uint4 hi = *reinterpret_cast<const uint4*>(sb + rb_hi + j * 16 * BK);
+        bf[j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      }
+      {
+        const uint4 lo = *reinterpret_cast<const uint4*>(sb + ra_lo);
+        const uint4 hi = *reinterpret_cast<const uint4*>(sb + ra_hi);
+        af[0] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      }
+      const float sbv = sbl_w[kb];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) sab[i] = *reinterpret_cast<const float*>(sb + rs + i * 16 * 4) * sbv;
+      __builtin_amdgcn_sched_barrier(0);
+      v4f p[3];
+#pragma unroll
+      for (int t = 0; t < 34; ++t) {
+        if (t < 32) {
+          const int i = t >> 2, j = t & 3;
+          p[t % 3] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[j], af[i & 1], v4f{0.f, 0.f, 0.f, 0.f},
+                                                                       0, 0, 0, 127, 0, 127);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (t < 28 && (t & 3) == 0) {
+          const int i = (t >> 2) + 1;
+          const uint4 lo = *reinterpret_cast<const uint4*>(sb + ra_lo + i * 16 * BK);
+          const uint4 hi = *reinterpret_cast<const uint4*>(sb + ra_hi + i * 16 * BK);
+          af[i & 1] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        }
+        if (t >= 2) {
+          const int u = t - 2;
+          const v4f& r = p[u % 3];
+          v4f& c = acc[u >> 2][u & 3];
+          const float sc = sab[u >> 2];
+          c[0] = fmaf(r[0], sc, c[0]);
+          c[1] = fmaf(r[1], sc, c[1]);
+          c[2] = fmaf(r[2], sc, c[2]);
+          c[3] = fmaf(r[3], sc, c[3]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+
+    block_barrier();          // every wave is done with the previous tile's LDS
+    {
+      float* sbl = reinterpret_cast<float*>(smem + kSBOff);
+      for (int t = tid; t < 2 * nkb; t += kThreads) {
+        const int half = t / nkb, kb = t % nkb;
+        const int64_t nbh = (n0 / 128 + half) < nblk ? (n0 / 128 + half) : (nblk - 1);
+        sbl[half * kMaxKb + kb] = SB[nbh * nkb + kb];
+      }
+    }
+    issue(0, 0);
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    // top of step kb: this wave's DMA of stage kb done, then the barrier makes it true for
+    // all waves (and publishes the weight scales) and proves every wave has finished
+    // reading the other buffer (step kb-1), which then receives stage kb+1
+    for (int kb = 0; kb < nkb; kb += 2) {
+      wait_vmcnt<0>();
+      block_barrier();
+      if (kb + 1 < nkb) issue(kb + 1, 1);
+      if (wave_live) compute(I0{}, kb);
+      if (kb + 1 >= nkb) break;
+      wait_vmcnt<0>();
+      block_barrier();
+      if (kb + 2 < nkb) issue(kb + 2, 0);
+      if (wave_live) compute(I1{}, kb + 1);
+    }
+
+    if (!wave_live) continue;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int64_t row = m0 + wm * 128 + 16 * i + l16;
+      if (row >= M) continue;
+      uint16_t* drow = D + row * ldd + n0 + wn * 64 + 4 * q;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t lo = (uint32_t)bf16_bits_rne(acc[i][j][0]) | ((uint32_t)bf16_bits_rne(acc[i][j][1]) << 16);
+        const uint32_t hi = (uint32_t)bf16_bits_rne(acc[i][j][2]) | ((uint32_t)bf16_bits_rne(acc[i][j][3]) << 16);
+        *reinterpret_cast<uint2*>(drow + 16 * j) = make_uint2(lo, hi);
+      }
+    }
+  }
+}
+
 hipError_t launch_gemm_fp8_contig(int32_t G, int64_t M, int64_t N, int64_t K, const uint8_t* a,
                                   const float* sa, const uint8_t* b, const float* sb,
                                   const int32_t* offsets, uint16_t* d, int64_t ldd, int num_cus,
                                   hipStream_t st) {
   if (M == 0 || N == 0) return hipSuccess;
   if (N % 128 != 0 || K % BK != 0) return hipErrorInvalidValue;
+  if (offsets == nullptr && G == 1 && K / BK <= dense::kMaxKb) {
+    // dense: 256 x 256 tiles, one workgroup per CU, a multiple of the XCD count
+    int64_t grid = (int64_t)num_cus;
+    grid = (grid / kXcds) * kXcds;
+    if (grid < kXcds * dense::kSM) grid = kXcds * dense::kSM;
+    hipLaunchKernelGGL(gemm_fp8_dense_kernel, dim3((unsigned)grid), dim3(dense::kThreads), 0, st, M, N, K, a, sa,
+                       b, sb, d, ldd);
+    return hipGetLastError();
+  }
   // one workgroup per CU, a multiple of the XCD count (the schedule assigns tiles per XCD)
   int64_t grid = (int64_t)num_cus;
   grid = (grid / kXcds) * kXcds;
