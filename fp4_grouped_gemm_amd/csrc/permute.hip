@@ -211,21 +211,27 @@ __global__ void __launch_bounds__(256) permute_gather_kernel(const int32_t* __re
 // scales and then gathering the codes (the permute_gather_kernel contract),
 // without writing or re-reading the token-order codes.  One wave per token:
 // lane j < k holds slot j's destination row; a token with no destination
-// below M_cap is not read at all.  The wave walks K in passes of 512 columns
-// (16 lanes x 8 elements per 128-column group), loading up to kPB passes
-// before using them, and writes each pass's codes and scales to every
-// destination row.  A second phase zero-fills the padding rows of [0, M_total).
+// below M_cap is not read at all.  The wave walks K in passes of 1024 columns
+// (8 lanes x 16 elements per 128-column group), loading kPB passes before
+// using them, and writes each pass's codes (16 bytes per lane) and scales to
+// every destination row.  A second phase zero-fills the padding rows of [0, M_total).
+// Raw bytes of 8 consecutive elements: one 16-byte load for bf16, two for fp32.
 template <bool BF16>
-struct RawRow8 {
-  uint4 a, b;   // b only for fp32 input
+struct RawRow8;
+template <>
+struct RawRow8<true> {
+  uint4 a;
+};
+template <>
+struct RawRow8<false> {
+  uint4 a, b;
 };
 
 template <bool BF16>
 __device__ inline RawRow8<BF16> load_raw8(const void* base, int64_t idx) {
   RawRow8<BF16> r;
-  if (BF16) {
+  if constexpr (BF16) {
     r.a = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(base) + idx);
-    r.b = make_uint4(0, 0, 0, 0);
   } else {
     const uint4* q = reinterpret_cast<const uint4*>(reinterpret_cast<const float*>(base) + idx);
     r.a = q[0];
@@ -236,7 +242,7 @@ __device__ inline RawRow8<BF16> load_raw8(const void* base, int64_t idx) {
 
 template <bool BF16>
 __device__ inline void unpack_raw8(const RawRow8<BF16>& r, float* f) {
-  if (BF16) {
+  if constexpr (BF16) {
     const uint32_t w[4] = {r.a.x, r.a.y, r.a.z, r.a.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -259,43 +265,48 @@ __global__ void __launch_bounds__(256) permute_quantize_kernel(const int32_t* __
                                                                 int64_t T, int64_t K,
                                                                 uint8_t* __restrict__ a_out,
                                                                 float* __restrict__ sa_out, int64_t M_cap) {
-  constexpr int kPB = 8;   // passes of 512 columns loaded together
-  const int lane = threadIdx.x & 63, sub = lane & 15;
+  constexpr int kPB = 4;   // passes of 1024 columns loaded together
+  const int lane = threadIdx.x & 63, sub = lane & 7;
   const int64_t wave_id = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int64_t nwaves = (int64_t)gridDim.x * 4;
   for (int64_t t = wave_id; t < T; t += nwaves) {
     const int32_t dst = lane < k ? src_to_row[t * k + lane] : -1;
     const uint64_t dmask = __ballot(dst >= 0 && dst < M_cap);
     if (dmask == 0) continue;
-    for (int64_t c0 = 0; c0 < K; c0 += 512 * kPB) {
-      RawRow8<BF16> raw[kPB];
+    for (int64_t c0 = 0; c0 < K; c0 += 1024 * kPB) {
+      RawRow8<BF16> raw[kPB][2];
 #pragma unroll
       for (int pb = 0; pb < kPB; ++pb) {
-        const int64_t col = c0 + 512 * pb + 8 * lane;
-        if (col < K) raw[pb] = load_raw8<BF16>(x, t * ldx + col);
+        const int64_t col = c0 + 1024 * pb + 16 * lane;
+        if (col < K) {
+          raw[pb][0] = load_raw8<BF16>(x, t * ldx + col);
+          raw[pb][1] = load_raw8<BF16>(x, t * ldx + col + 8);
+        }
       }
 #pragma unroll
       for (int pb = 0; pb < kPB; ++pb) {
-        const int64_t col = c0 + 512 * pb + 8 * lane;
-        if (c0 + 512 * pb >= K) break;              // wave-uniform
-        const bool live = col < K;                  // uniform per 16-lane group (K % 128 == 0)
-        float v[8];
+        const int64_t col = c0 + 1024 * pb + 16 * lane;
+        if (c0 + 1024 * pb >= K) break;             // wave-uniform
+        const bool live = col < K;                  // uniform per 8-lane group (K % 128 == 0)
+        float v[16];
         if (live) {
-          unpack_raw8<BF16>(raw[pb], v);
+          unpack_raw8<BF16>(raw[pb][0], v);
+          unpack_raw8<BF16>(raw[pb][1], v + 8);
         } else {
 #pragma unroll
-          for (int i = 0; i < 8; ++i) v[i] = 0.0f;
+          for (int i = 0; i < 16; ++i) v[i] = 0.0f;
         }
         float amax = 0.0f;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
-        amax = group_max<16>(amax);
+        for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(v[i]));
+        amax = group_max<8>(amax);
         const float s = (amax == 0.0f) ? 1.0f : amax / 448.0f;
         const float r = __builtin_amdgcn_rcpf(s);
-        float y[8];
+        float y[16];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) y[i] = e4m3_quotient(v[i], s, r);
-        const uint2 codes = make_uint2(e4m3_pack4(y[0], y[1], y[2], y[3]), e4m3_pack4(y[4], y[5], y[6], y[7]));
+        for (int i = 0; i < 16; ++i) y[i] = e4m3_quotient(v[i], s, r);
+        const uint4 codes = make_uint4(e4m3_pack4(y[0], y[1], y[2], y[3]), e4m3_pack4(y[4], y[5], y[6], y[7]),
+                                       e4m3_pack4(y[8], y[9], y[10], y[11]), e4m3_pack4(y[12], y[13], y[14], y[15]));
         const int64_t kb = col >> 7;
         uint64_t m = dmask;
         while (m) {
@@ -303,7 +314,7 @@ __global__ void __launch_bounds__(256) permute_quantize_kernel(const int32_t* __
           m &= m - 1;
           const int64_t row = __shfl(dst, j);
           if (live) {
-            *reinterpret_cast<uint2*>(a_out + row * K + col) = codes;
+            *reinterpret_cast<uint4*>(a_out + row * K + col) = codes;
             if (sub == 0) sa_out[kb * M_cap + row] = s;
           }
         }
