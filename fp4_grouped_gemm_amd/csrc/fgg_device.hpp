@@ -93,6 +93,20 @@ __device__ inline uint32_t e4m3_pack4(float v0, float v1, float v2, float v3) {
   return (uint32_t)w;
 }
 
+// e^-g from the hardware base-2 exponential: -g·log2(e) is formed as hi + lo
+// (log2(e) split into fp32 hi and lo parts, the product's rounding error
+// recovered with an FMA) and 2^(hi + lo) = 2^hi · (1 + lo·ln 2) to first order,
+// which keeps the result within a few ulps; overflow gives +inf, underflow 0.
+__device__ inline float exp_neg(float g) {
+  constexpr float kLog2eHi = 1.44269502162933349609375f;   // fp32 nearest to log2(e)
+  constexpr float kLog2eLo = 1.92596298909109e-08f;        // log2(e) - kLog2eHi
+  constexpr float kLn2 = 0.693147180559945309f;
+  const float x = -g * kLog2eHi;
+  const float x_lo = __builtin_fmaf(-g, kLog2eHi, -x) - g * kLog2eLo;
+  const float e = __builtin_amdgcn_exp2f(x);
+  return __builtin_fmaf(e, x_lo * kLn2, e);
+}
+
 // a / d for d >= 1 (SiLU denominators): reciprocal and one Newton step,
 // within about one ulp; d is clamped finite so that a huge denominator gives 0.
 __device__ inline float div_by_ge1(float a, float d) {

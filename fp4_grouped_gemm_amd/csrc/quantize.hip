@@ -43,7 +43,7 @@ __global__ void __launch_bounds__(256) quant_e4m3_1x128_kernel(const void* __res
         float u[8];
         load8<BF16>(x, row * ldx + cols + col, u);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) v[i] = div_by_ge1(v[i], 1.0f + expf(-v[i])) * u[i];
+        for (int i = 0; i < 8; ++i) v[i] = div_by_ge1(v[i], 1.0f + exp_neg(v[i])) * u[i];
       }
     } else {
 #pragma unroll
