@@ -77,6 +77,7 @@ def load_library():
         "fgg_moe_permute": ([P, I64, I32, I32, I32, P, P, I64, P, P, P, P, P, P, I64, P, SZ, P], I32),
         "fgg_moe_permute_quantize": ([P, I64, I32, I32, I32, P, I32, I64, I64, P, P, P, P, P, P, I64, P, SZ, P], I32),
         "fgg_grouped_gemm_scaled": ([I32, I32, I64, I64, I64, P, P, QDesc, P, P, QDesc, P, P, P, I64, P], I32),
+        "fgg_grouped_gemm_silu_quantize": ([I32, I64, I64, I64, P, P, QDesc, P, P, QDesc, P, P, P, P], I32),
         "fgg_scaled_gemm_workspace": ([I64, I64, I64, QDesc, QDesc, ctypes.POINTER(Epilogue), ctypes.POINTER(SZ)], I32),
         "fgg_scaled_gemm": ([I64, I64, I64, P, P, QDesc, P, P, QDesc, ctypes.POINTER(Epilogue), P, I64, P, SZ, P], I32),
         "fgg_moe_combine": ([P, I64, P, P, I64, I32, I64, P, I64, P], I32),
@@ -252,6 +253,28 @@ def grouped_gemm_scaled(a, a_scales, b, b_scales, offsets=None, masked_m=None,
         _ptr(offsets), _ptr(masked_m), _ptr(out), out.stride(-2), _stream(dev))
     _check("fgg_grouped_gemm_scaled", st)
     return out
+
+
+def grouped_gemm_silu_quantize(a, a_scales, b, b_scales, offsets, out=None, scales=None):
+    """Gate-up grouped GEMM with SiLU(gate)*up and the 1x128 e4m3 requantization
+    fused (fgg_grouped_gemm_silu_quantize): a [M, K] e4m3 with [K/128, M]
+    scales, b [G, 2I, K] ([gate | up] rows) with [G, 2I/128, K/128] scales.
+    Returns (codes uint8 [M, I], scales f32 [I/128, M])."""
+    G, N2, K = b.shape
+    I = N2 // 2
+    M = a.shape[0]
+    dev = a.device
+    for t in (a, a_scales, b, b_scales, offsets):
+        assert t.is_contiguous()
+    if out is None:
+        out = torch.empty((M, I), dtype=torch.uint8, device=dev)
+    if scales is None:
+        scales = torch.empty((I // 128, M), dtype=torch.float32, device=dev)
+    st = load_library().fgg_grouped_gemm_silu_quantize(
+        G, M, I, K, _ptr(a), _ptr(a_scales), _q(Q_E4M3_1x128), _ptr(b), _ptr(b_scales), _q(Q_E4M3_128x128),
+        _ptr(offsets), _ptr(out), _ptr(scales), _stream(dev))
+    _check("fgg_grouped_gemm_silu_quantize", st)
+    return out, scales
 
 
 def scaled_gemm_workspace_bytes(M: int, N: int, K: int, qdesc: str = "fp8", rank: int = 0) -> int:

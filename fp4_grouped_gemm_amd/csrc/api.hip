@@ -191,8 +191,8 @@ fgg_status fgg_grouped_gemm_scaled(fgg_layout layout, int32_t G, int64_t M, int6
     fgg_status st = device_check(&num_cus);
     if (st != FGG_OK) return st;
     if (debug_enabled())
-      std::fprintf(stderr, "[fgg] grouped_gemm contiguous G=%d M=%lld N=%lld K=%lld tile=128x128x128 stages=2 lds=%d B grid<=%d\n",
-                   G, (long long)M, (long long)N, (long long)K, 2 * (128 * 128 * 2 + 512), num_cus * 2);
+      std::fprintf(stderr, "[fgg] grouped_gemm contiguous G=%d M=%lld N=%lld K=%lld tile=128x256 (grouped) grid=%d\n",
+                   G, (long long)M, (long long)N, (long long)K, num_cus);
     if (M == 0 || N == 0) return FGG_OK;
     return finish(fgg::launch_gemm_fp8_contig(G, M, N, K, (const uint8_t*)a, (const float*)a_scales,
                                               (const uint8_t*)b, (const float*)b_scales, offsets, (uint16_t*)d,
@@ -211,6 +211,26 @@ fgg_status fgg_grouped_gemm_scaled(fgg_layout layout, int32_t G, int64_t M, int6
                                           (hipStream_t)stream));
   }
   return FGG_ERR_INVALID_VALUE;
+}
+
+fgg_status fgg_grouped_gemm_silu_quantize(int32_t G, int64_t M, int64_t I, int64_t K, const void* a,
+                                          const void* a_scales, fgg_qdesc aq, const void* b, const void* b_scales,
+                                          fgg_qdesc bq, const int32_t* offsets, void* q_out, float* s_out,
+                                          void* stream) {
+  if (G < 1 || G > 1024 || M < 0 || I < 0 || K < 0) return FGG_ERR_INVALID_VALUE;
+  if (I % 128 != 0 || K % 128 != 0 || K > 16384) return FGG_ERR_UNSUPPORTED;
+  if (!same_q(aq, FGG_E4M3, FGG_F32, 1, 128) || !same_q(bq, FGG_E4M3, FGG_F32, 128, 128)) return FGG_ERR_UNSUPPORTED;
+  if (!a || !a_scales || !b || !b_scales || !offsets || !q_out || !s_out) return FGG_ERR_INVALID_VALUE;
+  if (!aligned(a, 16) || !aligned(b, 16) || !aligned(q_out, 16) || !aligned(a_scales, 4) || !aligned(b_scales, 4) ||
+      !aligned(s_out, 4))
+    return FGG_ERR_INVALID_VALUE;
+  int num_cus = 0;
+  fgg_status st = device_check(&num_cus);
+  if (st != FGG_OK) return st;
+  if (M == 0 || I == 0) return FGG_OK;
+  return finish(fgg::launch_gemm_fp8_silu_quantize(G, M, I, K, (const uint8_t*)a, (const float*)a_scales,
+                                                   (const uint8_t*)b, (const float*)b_scales, offsets,
+                                                   (uint8_t*)q_out, s_out, num_cus, (hipStream_t)stream));
 }
 
 fgg_status fgg_scaled_gemm_workspace(int64_t M, int64_t N, int64_t K, fgg_qdesc aq, fgg_qdesc bq,

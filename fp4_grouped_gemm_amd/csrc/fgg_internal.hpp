@@ -37,6 +37,10 @@ hipError_t launch_gemm_fp8_contig(int32_t G, int64_t M, int64_t N, int64_t K, co
                                   hipStream_t st);
 
 // Masked (decode) layout, A e4m3 1x128; B either E2M1x2 + E8M0/32 or e4m3 128x128.
+hipError_t launch_gemm_fp8_silu_quantize(int32_t G, int64_t M, int64_t I, int64_t K, const uint8_t* a,
+                                         const float* sa, const uint8_t* b, const float* sb,
+                                         const int32_t* offsets, uint8_t* q, float* s, int num_cus,
+                                         hipStream_t st);
 hipError_t launch_gemm_masked(bool b_fp4, int32_t G, int64_t M, int64_t N, int64_t K,
                               const uint8_t* a, const float* sa, const uint8_t* b, const void* sb,
                               const int32_t* masked_m, uint16_t* d, int64_t ldd, hipStream_t st);

@@ -131,11 +131,18 @@ __device__ inline int find_group(const int32_t* __restrict__ offsets, int G, int
 
 }  // namespace
 
+// SILU: the gate-up GEMM with SiLU(gate)·up and the 1x128 e4m3 requantization in the
+// epilogue.  B has N = 2I rows ([gate | up]); the tile of output block j (128
+// columns of the activation) takes gate rows [128j, 128j+128) and up rows
+// [I+128j, I+128j+128) as its 256 columns, so each row's gate and up values meet in
+// one workgroup.  Writes Q [rows][I] e4m3 and S [I/128][M] fp32 instead of D.
+template <bool SILU>
 __global__ void __launch_bounds__(kThreads, 1)
 gemm_fp8_contig_kernel(int G, int64_t M, int64_t N, int64_t K, const uint8_t* __restrict__ A,
                        const float* __restrict__ SA, const uint8_t* __restrict__ B,
                        const float* __restrict__ SB, const int32_t* __restrict__ offsets,
-                       uint16_t* __restrict__ D, int64_t ldd) {
+                       uint16_t* __restrict__ D, int64_t ldd, uint8_t* __restrict__ Q,
+                       float* __restrict__ S) {
   __shared__ __align__(16) uint8_t smem[kLdsBytes];
   const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
   const int tid = threadIdx.x;
@@ -146,7 +153,9 @@ gemm_fp8_contig_kernel(int G, int64_t M, int64_t N, int64_t K, const uint8_t* __
 
   const int64_t m_end = offsets ? (int64_t)offsets[G] : M;
   const int64_t m_tiles = (m_end + BM - 1) / BM;
-  const int64_t n_tiles = (N + BN - 1) / BN;     // N % 128 == 0: a last tile may be half wide
+  // N % 128 == 0: a last tile may be half wide; with SILU, N = 2I and tile j covers
+  // gate block j and up block j (I / 128 tiles)
+  const int64_t n_tiles = SILU ? N / 256 : (N + BN - 1) / BN;
   const int nkb = (int)(K / BK);
   const int64_t nblk = N / 128;
 
@@ -184,7 +193,10 @@ gemm_fp8_contig_kernel(int G, int64_t M, int64_t N, int64_t K, const uint8_t* __
     const int64_t rows_here = (m_end - m0) < BM ? (m_end - m0) : BM;   // >= 1
     const int64_t cols_here = (N - n0) < BN ? (N - n0) : BN;           // 128 or 256
     const uint8_t* Atile = A + m0 * K;
-    const uint8_t* Btile = B + ((int64_t)g * N + n0) * K;
+    // this wave's B DMA rows are tile rows [32 * wave, 32 * wave + 32): with SILU, waves
+    // 0-3 fetch gate rows and waves 4-7 up rows, each from its own base
+    const int64_t b_first = SILU ? (wave < 4 ? nt * 128 : N / 2 + nt * 128 - 128) : n0;
+    const uint8_t* Btile = B + ((int64_t)g * N + b_first) * K;
 
     // per-lane byte offsets (within the tile) of this wave's DMA rows; rows past the
     // end of A are redirected to the last valid row (their outputs are never stored)
@@ -348,7 +360,8 @@ gemm_fp8_contig_kernel(int G, int64_t M, int64_t N, int64_t K, const uint8_t* __
       float* sbl = reinterpret_cast<float*>(smem + kSBOff);
       for (int t = tid; t < 2 * nkb; t += kThreads) {
         const int half = t / nkb, kb = t % nkb;
-        const int64_t nbh = (n0 / 128 + half) < nblk ? (n0 / 128 + half) : (nblk - 1);
+        int64_t nbh = SILU ? (half ? nblk / 2 + nt : nt) : n0 / 128 + half;
+        if (nbh >= nblk) nbh = nblk - 1;
         sbl[half * kMaxKb + kb] = SB[((int64_t)g * nblk + nbh) * nkb + kb];
       }
     }
@@ -375,6 +388,47 @@ gemm_fp8_contig_kernel(int G, int64_t M, int64_t N, int64_t K, const uint8_t* __
       if (kb + 5 < nkb) step(I2{}, f1, f0, kb + 5);
     }
 
+    if constexpr (SILU) {
+      // Stage the fp32 tile in LDS (rows padded to 1040 bytes), then 16 threads per
+      // row and 128-column group: a = SiLU(gate) * up on the fp32 values, the group
+      // maximum, s = max / 448 and the e4m3 codes (the rule of the 1x128 quantizer).
+      constexpr int kRowF = 260;                   // floats per staged row (1040 bytes)
+      float* stage = reinterpret_cast<float*>(smem);
+      __builtin_amdgcn_s_waitcnt(kLgkmZero);
+      block_barrier();                             // every wave is done with the K loop's LDS
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < kNFrag; ++j)
+          *reinterpret_cast<v4f*>(stage + (wm * 64 + 16 * i + l16) * kRowF + wn * kWaveCols + 16 * j + 4 * q) =
+              acc[i][j];
+      __syncthreads();
+      const int64_t I = N / 2;
+      for (int item = tid; item < BM * 16; item += kThreads) {
+        const int r = item >> 4, t16 = item & 15;
+        const bool live = r < rows_here;
+        float a[8];
+        const float* gp = stage + r * kRowF + 8 * t16;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) a[e] = div_by_ge1(gp[e], 1.0f + exp_neg(gp[e])) * gp[128 + e];
+        float amax = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(a[e]));
+        amax = group_max<16>(amax);
+        const float sc = (amax == 0.0f) ? 1.0f : amax / 448.0f;
+        const float rc = __builtin_amdgcn_rcpf(sc);
+        float y[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) y[e] = e4m3_quotient(a[e], sc, rc);
+        if (live) {
+          const int64_t row = m0 + r;
+          *reinterpret_cast<uint2*>(Q + row * I + nt * 128 + 8 * t16) =
+              make_uint2(e4m3_pack4(y[0], y[1], y[2], y[3]), e4m3_pack4(y[4], y[5], y[6], y[7]));
+          if (t16 == 0) S[nt * M + row] = sc;
+        }
+      }
+      continue;                                    // the next tile starts with a barrier
+    }
     // epilogue: lane holds columns n0 + wn*64 + 16j + 4q + (0..3) of row m0 + wm*64 + 16i + l16
     if (wn * kWaveCols >= cols_here) continue;
 #pragma unroll
@@ -617,8 +671,22 @@ hipError_t launch_gemm_fp8_contig(int32_t G, int64_t M, int64_t N, int64_t K, co
   int64_t grid = (int64_t)num_cus;
   grid = (grid / kXcds) * kXcds;
   if (grid < kXcds * kSM) grid = kXcds * kSM;
-  hipLaunchKernelGGL(gemm_fp8_contig_kernel, dim3((unsigned)grid), dim3(kThreads), 0, st, G, M, N, K, a, sa, b,
-                     sb, offsets, d, ldd);
+  hipLaunchKernelGGL(gemm_fp8_contig_kernel<false>, dim3((unsigned)grid), dim3(kThreads), 0, st, G, M, N, K, a,
+                     sa, b, sb, offsets, d, ldd, nullptr, nullptr);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_fp8_silu_quantize(int32_t G, int64_t M, int64_t I, int64_t K, const uint8_t* a,
+                                         const float* sa, const uint8_t* b, const float* sb,
+                                         const int32_t* offsets, uint8_t* q, float* s, int num_cus,
+                                         hipStream_t st) {
+  if (M == 0 || I == 0) return hipSuccess;
+  if (I % 128 != 0 || K % BK != 0 || K / BK > kMaxKb) return hipErrorInvalidValue;
+  int64_t grid = (int64_t)num_cus;
+  grid = (grid / kXcds) * kXcds;
+  if (grid < kXcds * kSM) grid = kXcds * kSM;
+  hipLaunchKernelGGL(gemm_fp8_contig_kernel<true>, dim3((unsigned)grid), dim3(kThreads), 0, st, G, M, 2 * I, K, a,
+                     sa, b, sb, offsets, nullptr, (int64_t)0, q, s);
   return hipGetLastError();
 }
 

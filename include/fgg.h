@@ -212,6 +212,32 @@ fgg_status fgg_grouped_gemm_scaled(fgg_layout layout, int32_t G, int64_t M, int6
                                    int64_t ldd, void* stream);
 
 /*
+ * fgg_grouped_gemm_silu_quantize — the gate-up grouped GEMM (contiguous layout)
+ * with SiLU(gate)·up and the 1x128 e4m3 requantization fused into its epilogue.
+ *
+ * [MegaMoE] §3.1 fuses the gate GEMM with its Swish activation so that the
+ * intermediate never goes to memory; [Infra] Q "量化矩阵乘的维度和流程": the
+ * next GEMM's input is quantized online.  B holds both projections of each
+ * expert: b [G][2I][K] e4m3 (rows [0, I) gate, [I, 2I) up) with b_scales
+ * [G][2I/128][K/128]; a, a_scales, offsets and their rules are those of
+ * fgg_grouped_gemm_scaled CONTIGUOUS.  For every row r < offsets[G]:
+ *   h[r][n] = Σ_kb sA[kb][r] · sB[g][n/128][kb] · Σ_{k in kb} A[r][k]·B[g][n][k]   (fp32, not rounded)
+ *   a[r][c] = h[r][c] / (1 + e^-h[r][c]) · h[r][I + c]
+ *   q_out[r][c], s_out[c/128][r] = the 1x128 e4m3 quantization of a (the rule of
+ *   fgg_quantize_blockwise: s = max|a| / 448 per 128 columns, codes = RNE(a / s))
+ * q_out is [M][I] bytes, s_out [I/128][M] fp32 (K-block-major, the activation
+ * layout of the down GEMM).  Rows >= offsets[G] are not written.  The
+ * separate path (bf16 H from fgg_grouped_gemm_scaled, then
+ * fgg_quantize_blockwise with FGG_ACT_SILU_MUL) rounds H to bf16 first, so the
+ * two may differ by one code where a value sits at a rounding boundary.
+ * Requirements: I % 128 == 0, K % 128 == 0, K <= 16384, 1 <= G <= 1024.
+ */
+fgg_status fgg_grouped_gemm_silu_quantize(int32_t G, int64_t M, int64_t I, int64_t K, const void* a,
+                                          const void* a_scales, fgg_qdesc aq, const void* b, const void* b_scales,
+                                          fgg_qdesc bq, const int32_t* offsets, void* q_out, float* s_out,
+                                          void* stream);
+
+/*
  * fgg_scaled_gemm — the dense one-group case ([MegaMoE] §2.1 fp8_gemm with
  * fine-grained scales), and the W4A4 operator of [W4A4] §1.
  *

@@ -31,3 +31,23 @@ def cuda(x, dtype=None):
     if dtype is not None:
         t = t.to(dtype)
     return t.cuda()
+
+
+def codes_close(q, q_ref, s, s_ref, rtol, min_equal=0.999, max_step=1, what=""):
+    """The several-correct-answers bar for e4m3 codes computed from values that
+    carry rounding differences: scales within rtol, at least min_equal of the
+    codes identical, and every other code with the same sign (or one side zero)
+    and at most max_step steps away in the code order (max_step None: not
+    checked, for inputs that differ by more than rounding)."""
+    q = np.asarray(q); q_ref = np.asarray(q_ref)
+    assert q.shape == q_ref.shape, (q.shape, q_ref.shape)
+    np.testing.assert_allclose(s, s_ref, rtol=rtol, atol=0, err_msg=what)
+    same = q == q_ref
+    assert same.mean() >= min_equal, f"{what}: only {same.mean():.5f} of the codes equal"
+    mism = ~same
+    if mism.any():
+        a, b = q[mism].astype(int), q_ref[mism].astype(int)
+        zero = ((a & 0x7F) == 0) | ((b & 0x7F) == 0)
+        assert np.all(((a & 0x80) == (b & 0x80)) | zero), f"{what}: sign flips"
+        if max_step is not None:
+            assert np.all(np.abs((a & 0x7F) - (b & 0x7F)) <= max_step), f"{what}: codes more than {max_step} step apart"

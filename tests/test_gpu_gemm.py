@@ -14,7 +14,7 @@ import fp4_grouped_gemm_amd as fgg
 import oracle
 import synth
 from oracle import formats as F
-from _util import cuda, to_np, tol_check
+from _util import codes_close, cuda, to_np, tol_check
 
 pytestmark = pytest.mark.gpu
 
@@ -385,3 +385,86 @@ def test_w4a4_lowrank_branch_alone(M, N, K):
         np.ones((N, K // 16), np.float32), wl["x"], synth.to_bf16_values(ld), wl["l_up"], wl["bias"]))
     assert np.abs(ref).max() > 0.1                  # the branch is really exercised
     tol_check(to_np(y), ref, what="w4a4 low-rank branch")
+
+
+# ------------------------------------------------- fused gate-up + SiLU requant
+
+def _silu_requant_close(q, s, q_r, s_r, h_ref, what):
+    """Fused gate-up + SiLU requant against the oracle on the exact fp64 GEMM.
+    The GPU's fp32 GEMM result differs from the exact one within the library's
+    GEMM tolerance (large relative errors only where terms cancel to a tiny
+    value), so the codes are compared after dequantization: both sides' half-step
+    quantization error (2^-4 relative, 2^-10 of the scale near zero) plus that
+    tolerance carried through SiLU(gate)*up.  Scales (group maxima) agree to
+    2e-4 relative and almost every code is identical."""
+    codes_close(q, q_r, s, s_r, rtol=2e-4, min_equal=0.995, max_step=None, what=what)
+    a_ref = oracle.silu_mul(h_ref)
+    rms = float(np.sqrt(np.mean(a_ref ** 2)))
+    s_full, s_r_full = np.repeat(s, 128, axis=1), np.repeat(s_r, 128, axis=1)
+    deq = F.decode_e4m3(q) * s_full
+    deq_r = F.decode_e4m3(q_r) * s_r_full
+    bound = 2.0 ** -3 * np.abs(a_ref) + 2.0 ** -9 * s_r_full + 1e-2 * (np.abs(a_ref) + rms)
+    bad = np.abs(deq - deq_r) > bound
+    assert not bad.any(), f"{what}: {int(bad.sum())} dequantized values outside tolerance"
+
+
+@pytest.mark.parametrize("counts,I,K", [([5, 0, 300, 128], 128, 512), ([1], 128, 128), ([129, 1000], 256, 1024)])
+def test_grouped_silu_quantize_small(counts, I, K):
+    x, w, offsets = _contig_case(len(counts) * 17 + I + K, counts, 2 * I, K)
+    xq, xs = fgg.quantize_blockwise(cuda(x), fgg.Q_E4M3_1x128)
+    bq, sb = _quant_weights_gpu(w, fgg.Q_E4M3_128x128)
+    M = x.shape[0]
+    q = torch.full((M, I), 0xAB, dtype=torch.uint8, device="cuda")
+    s = torch.full((I // 128, M), -3.0, dtype=torch.float32, device="cuda")
+    fgg.grouped_gemm_silu_quantize(xq, xs, bq, sb, cuda(offsets), out=q, scales=s)
+    q, s = to_np(q), to_np(s)
+    aq_r, sa_r = oracle.quantize_e4m3_blocks(x, 1, 128)
+    bq_r, sb_r = _quant_weights_oracle(w)
+    mt = int(offsets[-1])
+    h = oracle.grouped_gemm_contiguous(aq_r, sa_r, bq_r, sb_r, offsets)[:mt]   # fp64, not rounded
+    q_r, s_r = oracle.silu_mul_quantize(h)
+    _silu_requant_close(q[:mt], s[:, :mt].T, q_r, s_r, h, "fused gate-up SiLU requant")
+    assert np.all(q[mt:] == 0xAB) and np.all(s[:, mt:] == -3.0)       # rows >= offsets[G] untouched
+    for e in range(len(counts)):                                      # padding rows: zero codes, scale 1
+        lo, hi = offsets[e] + counts[e], offsets[e + 1]
+        assert np.all(q[lo:hi] == 0) and np.all(s[:, lo:hi] == 1.0)
+
+
+def test_grouped_silu_quantize_prefill_matches_separate_path():
+    """Full prefill gate-up shape: the fused kernel against the separate GEMM +
+    SiLU requant (bf16 H in between), and sampled rows against the oracle."""
+    cfg = synth.MOE_PREFILL
+    T, K, E, k, Ngu = cfg["T"], cfg["K"], cfg["E"], cfg["k"], cfg["N_gu"]
+    r = synth.moe_prefill_routing()
+    x = synth.moe_prefill_x()
+    perm = fgg.moe_permute(cuda(r["topk_ids"]), E, 128, x=cuda(x, torch.bfloat16))
+    gu_q, gu_s = [], []
+    keep = {}
+    for e in range(E):
+        wgu = synth.moe_prefill_expert_weight(1003, "gu", e, Ngu, K)
+        qq, ss = fgg.quantize_blockwise(cuda(wgu), fgg.Q_E4M3_128x128)
+        gu_q.append(qq); gu_s.append(ss)
+        if e in (3, 30):
+            keep[e] = wgu
+    gu_q, gu_s = torch.stack(gu_q), torch.stack(gu_s)
+    offs = perm["offsets"]
+    q, s = fgg.grouped_gemm_silu_quantize(perm["a"], perm["sa"], gu_q, gu_s, offs)
+    h = fgg.grouped_gemm_scaled(perm["a"], perm["sa"], gu_q, gu_s, offsets=offs)
+    q2, s2 = fgg.quantize_blockwise(h, fgg.Q_E4M3_1x128, silu_mul=True, rows_dev=offs[E:])
+    mt = int(to_np(offs)[E])
+    q, s, q2, s2 = to_np(q)[:mt], to_np(s)[:, :mt], to_np(q2)[:mt], to_np(s2)[:, :mt]
+    # the separate path rounds gate and up to bf16 (each within 2^-9 relative) before
+    # SiLU, whose relative sensitivity d ln SiLU(g) / d ln g = 1 + g (1 - sigmoid(g))
+    # grows to |1 + g| for negative g: scales agree to ~1%, codes to one step, and a
+    # few percent of the codes sit across a rounding boundary
+    codes_close(q, q2, s.T, s2.T, rtol=2e-2, min_equal=0.9, max_step=1, what="fused vs separate path")
+    offsets = to_np(offs).astype(np.int64)
+    counts = to_np(perm["counts"])
+    a_all, sa_all = to_np(perm["a"]), to_np(perm["sa"])
+    for e, wgu in keep.items():
+        rows = offsets[e] + np.unique(np.linspace(0, counts[e] - 1, 5).astype(np.int64))
+        bq_r, sb_r = oracle.quantize_e4m3_blocks(wgu, 128, 128)
+        h_r = oracle.grouped_gemm_contiguous(a_all[rows], sa_all[:, rows].T, bq_r[None], sb_r[None],
+                                             np.array([0, len(rows)]))
+        q_r, s_r = oracle.silu_mul_quantize(h_r)
+        _silu_requant_close(q[rows], s[:, rows].T, q_r, s_r, h_r, f"fused gate-up expert {e}")
