@@ -121,13 +121,15 @@ def prefill_step(fgg, st, t_gu=None, t_dn=None):
     if t_gu:
         t_gu.start()
     # gate-up grouped GEMM with SiLU(gate)*up and the 1x128 e4m3 requantization in its epilogue
-    fgg.grouped_gemm_silu_quantize(p["a"], p["sa"], st["gu_q"], st["gu_s"], p["offsets"], out=b["a2"],
-                                   scales=b["s2"])
+    # (the permute's counts let both GEMMs skip the padding rows of each expert segment)
+    fgg.grouped_gemm_silu_quantize(p["a"], p["sa"], st["gu_q"], st["gu_s"], p["offsets"], counts=p["counts"],
+                                   out=b["a2"], scales=b["s2"])
     if t_gu:
         t_gu.stop()
     if t_dn:
         t_dn.start()
-    fgg.grouped_gemm_scaled(b["a2"], b["s2"], st["dn_q"], st["dn_s"], offsets=p["offsets"], out=b["y"])
+    fgg.grouped_gemm_scaled(b["a2"], b["s2"], st["dn_q"], st["dn_s"], offsets=p["offsets"], masked_m=p["counts"],
+                            out=b["y"])
     if t_dn:
         t_dn.stop()
     fgg.moe_combine(b["y"], p["src_to_row"], st["tw"], out=b["out"])

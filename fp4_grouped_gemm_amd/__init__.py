@@ -77,7 +77,7 @@ def load_library():
         "fgg_moe_permute": ([P, I64, I32, I32, I32, P, P, I64, P, P, P, P, P, P, I64, P, SZ, P], I32),
         "fgg_moe_permute_quantize": ([P, I64, I32, I32, I32, P, I32, I64, I64, P, P, P, P, P, P, I64, P, SZ, P], I32),
         "fgg_grouped_gemm_scaled": ([I32, I32, I64, I64, I64, P, P, QDesc, P, P, QDesc, P, P, P, I64, P], I32),
-        "fgg_grouped_gemm_silu_quantize": ([I32, I64, I64, I64, P, P, QDesc, P, P, QDesc, P, P, P, P], I32),
+        "fgg_grouped_gemm_silu_quantize": ([I32, I64, I64, I64, P, P, QDesc, P, P, QDesc, P, P, P, P, P], I32),
         "fgg_scaled_gemm_workspace": ([I64, I64, I64, QDesc, QDesc, ctypes.POINTER(Epilogue), ctypes.POINTER(SZ)], I32),
         "fgg_scaled_gemm": ([I64, I64, I64, P, P, QDesc, P, P, QDesc, ctypes.POINTER(Epilogue), P, I64, P, SZ, P], I32),
         "fgg_moe_combine": ([P, I64, P, P, I64, I32, I64, P, I64, P], I32),
@@ -232,8 +232,10 @@ def grouped_gemm_scaled(a, a_scales, b, b_scales, offsets=None, masked_m=None,
     """Contiguous layout when ``offsets`` is given (a [M, K], a_scales [K/128, M],
     b [G, N, K], b_scales [G, N/128, K/128]); masked layout when ``masked_m``
     is given (a [G, M, K], a_scales [G, K/128, M], b [G, N, K/2] with E8M0
-    scales [G, N, K/32] for Q_E2M1_E8M0_1x32, or e4m3 as above).  Returns
-    bf16 [M, N] or [G, M, N]."""
+    scales [G, N, K/32] for Q_E2M1_E8M0_1x32, or e4m3 as above).  With
+    ``offsets``, an optional ``masked_m`` gives each group's real row count
+    (the permute's counts): the padding rows past it are not written.
+    Returns bf16 [M, N] or [G, M, N]."""
     G, N = b.shape[0], b.shape[1]
     dev = a.device
     if offsets is not None:
@@ -255,11 +257,12 @@ def grouped_gemm_scaled(a, a_scales, b, b_scales, offsets=None, masked_m=None,
     return out
 
 
-def grouped_gemm_silu_quantize(a, a_scales, b, b_scales, offsets, out=None, scales=None):
+def grouped_gemm_silu_quantize(a, a_scales, b, b_scales, offsets, counts=None, out=None, scales=None):
     """Gate-up grouped GEMM with SiLU(gate)*up and the 1x128 e4m3 requantization
     fused (fgg_grouped_gemm_silu_quantize): a [M, K] e4m3 with [K/128, M]
     scales, b [G, 2I, K] ([gate | up] rows) with [G, 2I/128, K/128] scales.
-    Returns (codes uint8 [M, I], scales f32 [I/128, M])."""
+    ``counts`` (optional, [G] int32): real rows per group; padding rows past
+    them are not written.  Returns (codes uint8 [M, I], scales f32 [I/128, M])."""
     G, N2, K = b.shape
     I = N2 // 2
     M = a.shape[0]
@@ -272,7 +275,7 @@ def grouped_gemm_silu_quantize(a, a_scales, b, b_scales, offsets, out=None, scal
         scales = torch.empty((I // 128, M), dtype=torch.float32, device=dev)
     st = load_library().fgg_grouped_gemm_silu_quantize(
         G, M, I, K, _ptr(a), _ptr(a_scales), _q(Q_E4M3_1x128), _ptr(b), _ptr(b_scales), _q(Q_E4M3_128x128),
-        _ptr(offsets), _ptr(out), _ptr(scales), _stream(dev))
+        _ptr(offsets), _ptr(counts), _ptr(out), _ptr(scales), _stream(dev))
     _check("fgg_grouped_gemm_silu_quantize", st)
     return out, scales
 

@@ -195,8 +195,8 @@ fgg_status fgg_grouped_gemm_scaled(fgg_layout layout, int32_t G, int64_t M, int6
                    G, (long long)M, (long long)N, (long long)K, num_cus);
     if (M == 0 || N == 0) return FGG_OK;
     return finish(fgg::launch_gemm_fp8_contig(G, M, N, K, (const uint8_t*)a, (const float*)a_scales,
-                                              (const uint8_t*)b, (const float*)b_scales, offsets, (uint16_t*)d,
-                                              ldd, num_cus, (hipStream_t)stream));
+                                              (const uint8_t*)b, (const float*)b_scales, offsets, masked_m,
+                                              (uint16_t*)d, ldd, num_cus, (hipStream_t)stream));
   }
   if (layout == FGG_LAYOUT_MASKED) {
     const bool fp4 = same_q(bq, FGG_E2M1X2, FGG_E8M0, 1, 32);
@@ -215,8 +215,8 @@ fgg_status fgg_grouped_gemm_scaled(fgg_layout layout, int32_t G, int64_t M, int6
 
 fgg_status fgg_grouped_gemm_silu_quantize(int32_t G, int64_t M, int64_t I, int64_t K, const void* a,
                                           const void* a_scales, fgg_qdesc aq, const void* b, const void* b_scales,
-                                          fgg_qdesc bq, const int32_t* offsets, void* q_out, float* s_out,
-                                          void* stream) {
+                                          fgg_qdesc bq, const int32_t* offsets, const int32_t* counts, void* q_out,
+                                          float* s_out, void* stream) {
   if (G < 1 || G > 1024 || M < 0 || I < 0 || K < 0) return FGG_ERR_INVALID_VALUE;
   if (I % 128 != 0 || K % 128 != 0 || K > 16384) return FGG_ERR_UNSUPPORTED;
   if (!same_q(aq, FGG_E4M3, FGG_F32, 1, 128) || !same_q(bq, FGG_E4M3, FGG_F32, 128, 128)) return FGG_ERR_UNSUPPORTED;
@@ -229,7 +229,7 @@ fgg_status fgg_grouped_gemm_silu_quantize(int32_t G, int64_t M, int64_t I, int64
   if (st != FGG_OK) return st;
   if (M == 0 || I == 0) return FGG_OK;
   return finish(fgg::launch_gemm_fp8_silu_quantize(G, M, I, K, (const uint8_t*)a, (const float*)a_scales,
-                                                   (const uint8_t*)b, (const float*)b_scales, offsets,
+                                                   (const uint8_t*)b, (const float*)b_scales, offsets, counts,
                                                    (uint8_t*)q_out, s_out, num_cus, (hipStream_t)stream));
 }
 
@@ -261,8 +261,8 @@ fgg_status fgg_scaled_gemm(int64_t M, int64_t N, int64_t K, const void* a, const
     if (st != FGG_OK) return st;
     if (M == 0 || N == 0) return FGG_OK;
     return finish(fgg::launch_gemm_fp8_contig(1, M, N, K, (const uint8_t*)a, (const float*)a_scales,
-                                              (const uint8_t*)b, (const float*)b_scales, nullptr, (uint16_t*)d,
-                                              ldd, num_cus, (hipStream_t)stream));
+                                              (const uint8_t*)b, (const float*)b_scales, nullptr, nullptr,
+                                              (uint16_t*)d, ldd, num_cus, (hipStream_t)stream));
   }
   if (same_q(aq, FGG_E2M1X2, FGG_F32, 1, 16) && same_q(bq, FGG_E2M1X2, FGG_F32, 1, 16)) {
     if (M % 128 != 0) return FGG_ERR_UNSUPPORTED;

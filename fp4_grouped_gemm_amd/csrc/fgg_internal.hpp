@@ -30,17 +30,20 @@ hipError_t launch_combine(const uint16_t* y, int64_t ldy, const int32_t* src_to_
                           hipStream_t st);
 
 // FP8 x FP8 grouped GEMM, contiguous layout (dense = one group with offsets {0, M}).
-// If offsets == nullptr the single group covers rows [0, M).
+// If offsets == nullptr the single group covers rows [0, M).  valid (nullable, with
+// offsets only): per-group row counts; rows past offsets[g] + valid[g] are padding.
 hipError_t launch_gemm_fp8_contig(int32_t G, int64_t M, int64_t N, int64_t K, const uint8_t* a,
                                   const float* sa, const uint8_t* b, const float* sb,
-                                  const int32_t* offsets, uint16_t* d, int64_t ldd, int num_cus,
-                                  hipStream_t st);
+                                  const int32_t* offsets, const int32_t* valid, uint16_t* d, int64_t ldd,
+                                  int num_cus, hipStream_t st);
 
-// Masked (decode) layout, A e4m3 1x128; B either E2M1x2 + E8M0/32 or e4m3 128x128.
+// The gate-up grouped GEMM with the SiLU(gate)*up 1x128 e4m3 requantization epilogue.
 hipError_t launch_gemm_fp8_silu_quantize(int32_t G, int64_t M, int64_t I, int64_t K, const uint8_t* a,
                                          const float* sa, const uint8_t* b, const float* sb,
-                                         const int32_t* offsets, uint8_t* q, float* s, int num_cus,
-                                         hipStream_t st);
+                                         const int32_t* offsets, const int32_t* valid, uint8_t* q, float* s,
+                                         int num_cus, hipStream_t st);
+
+// Masked (decode) layout, A e4m3 1x128; B either E2M1x2 + E8M0/32 or e4m3 128x128.
 hipError_t launch_gemm_masked(bool b_fp4, int32_t G, int64_t M, int64_t N, int64_t K,
                               const uint8_t* a, const float* sa, const uint8_t* b, const void* sb,
                               const int32_t* masked_m, uint16_t* d, int64_t ldd, hipStream_t st);

@@ -120,6 +120,14 @@ __device__ inline void wait_vmcnt() {
 
 __device__ inline void block_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
+// The value of x, hidden from the optimizer: address arithmetic derived from it is
+// computed where it is used (in a tile's epilogue) instead of being hoisted out of
+// the tile loop and held, or spilled, across the K loop.
+__device__ inline int opaque(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
 __device__ inline int find_group(const int32_t* __restrict__ offsets, int G, int64_t row) {
   int lo = 0, hi = G - 1;           // largest g with offsets[g] <= row
   while (lo < hi) {
@@ -141,14 +149,17 @@ __global__ void __launch_bounds__(kThreads, 1)
 gemm_fp8_contig_kernel(int G, int64_t M, int64_t N, int64_t K, const uint8_t* __restrict__ A,
                        const float* __restrict__ SA, const uint8_t* __restrict__ B,
                        const float* __restrict__ SB, const int32_t* __restrict__ offsets,
-                       uint16_t* __restrict__ D, int64_t ldd, uint8_t* __restrict__ Q,
-                       float* __restrict__ S) {
+                       const int32_t* __restrict__ valid, uint16_t* __restrict__ D, int64_t ldd,
+                       uint8_t* __restrict__ Q, float* __restrict__ S) {
   __shared__ __align__(16) uint8_t smem[kLdsBytes];
   const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave & 1, wn = wave >> 1;      // 2 waves along M, kWavesN along N
+  // 2 waves along M, kWavesN along N; waves w and w + 4 share a SIMD and take the two
+  // row halves of one column strip, so a tile whose lower half is padding leaves one
+  // busy wave on every SIMD rather than two on half of them
+  const int wm = wave >> 2, wn = wave & 3;
   const int l16 = lane & 15, q = lane >> 4;
 
   const int64_t m_end = offsets ? (int64_t)offsets[G] : M;
@@ -158,11 +169,6 @@ gemm_fp8_contig_kernel(int G, int64_t M, int64_t N, int64_t K, const uint8_t* __
   const int64_t n_tiles = SILU ? N / 256 : (N + BN - 1) / BN;
   const int nkb = (int)(K / BK);
   const int64_t nblk = N / 128;
-
-  // DMA lane roles: lane l fills 16-byte LDS chunk (l % 8) of row (l / 8) of an 8-row group;
-  // it reads source chunk (l % 8) ^ swz(row), where swz(row) = (l / 8) ^ (row-group index & 1).
-  const int lrow = lane >> 3;
-  const int lchunk = (lane & 7) ^ lrow;
 
   // Loop-invariant LDS read offsets (stage 0) of this lane's operand fragments:
   // fragment i is 16 rows (2048 bytes) further, stage s adds s * k{A,S,B}Bytes.
@@ -191,6 +197,18 @@ gemm_fp8_contig_kernel(int G, int64_t M, int64_t N, int64_t K, const uint8_t* __
     const int64_t m0 = mt * BM, n0 = nt * BN;
     const int g = offsets ? find_group(offsets, G, m0) : 0;
     const int64_t rows_here = (m_end - m0) < BM ? (m_end - m0) : BM;   // >= 1
+    // rows of the tile that are computed and stored: with per-group valid counts, a
+    // segment's rows past offsets[g] + valid[g] are padding (neither computed nor stored)
+    int64_t rows_valid = rows_here;
+    if (valid != nullptr) {
+      const int64_t seg0 = offsets[g], seg_len = (int64_t)offsets[g + 1] - seg0;
+      int64_t v = valid[g];
+      v = v < 0 ? 0 : (v > seg_len ? seg_len : v);
+      if (seg0 + v - m0 < rows_valid) rows_valid = seg0 + v - m0;
+      if (rows_valid <= 0) continue;               // the whole tile is padding (uniform)
+    }
+    // a wave whose 64 rows are all padding only helps move data
+    const bool busy = wm * 64 < rows_valid;
     const int64_t cols_here = (N - n0) < BN ? (N - n0) : BN;           // 128 or 256
     const uint8_t* Atile = A + m0 * K;
     // this wave's B DMA rows are tile rows [32 * wave, 32 * wave + 32): with SILU, waves
@@ -198,27 +216,33 @@ gemm_fp8_contig_kernel(int G, int64_t M, int64_t N, int64_t K, const uint8_t* __
     const int64_t b_first = SILU ? (wave < 4 ? nt * 128 : N / 2 + nt * 128 - 128) : n0;
     const uint8_t* Btile = B + ((int64_t)g * N + b_first) * K;
 
-    // per-lane byte offsets (within the tile) of this wave's DMA rows; rows past the
-    // end of A are redirected to the last valid row (their outputs are never stored)
+    // DMA lane roles: lane l fills 16-byte LDS chunk (l % 8) of row (l / 8) of an 8-row group;
+    // it reads source chunk (l % 8) ^ swz(row), where swz(row) = (l / 8) ^ (row-group index & 1).
+    // Per-lane byte offsets (within the tile) of this wave's DMA rows; rows past the
+    // end of A are redirected to the last valid row (their outputs are never stored).
+    // 32-bit arithmetic on per-tile lane values (nothing hoisted, nothing spilled).
+    const int lane_t = opaque(lane);
+    const int lrow = lane_t >> 3, lchunk = (lane_t & 7) ^ lrow;
+    const int rh = (int)rows_here, ch = (int)cols_here;
     uint32_t offA[kADma], offB[kBDma];
 #pragma unroll
     for (int i = 0; i < kADma; ++i) {
       const int grp8 = wave * kADma + i;             // 8-row group of the A tile
       int row = grp8 * 8 + lrow;
       const int c = lchunk ^ (grp8 & 1);
-      if (row >= rows_here) row = (int)rows_here - 1;
-      offA[i] = (uint32_t)(row * K + c * 16);
+      if (row >= rh) row = rh - 1;
+      offA[i] = (uint32_t)row * (uint32_t)K + (uint32_t)(c * 16);
     }
 #pragma unroll
     for (int i = 0; i < kBDma; ++i) {
       const int grp8 = wave * kBDma + i;
       int row = grp8 * 8 + lrow;
       const int c = lchunk ^ (grp8 & 1);
-      if (row >= cols_here) row = (int)cols_here - 1;   // half-wide last tile: stay inside B
-      offB[i] = (uint32_t)(row * K + c * 16);
+      if (row >= ch) row = ch - 1;                   // half-wide last tile: stay inside B
+      offB[i] = (uint32_t)row * (uint32_t)K + (uint32_t)(c * 16);
     }
-    int srow = wave * kSRows + (lane % kSRows);
-    if (srow >= rows_here) srow = (int)rows_here - 1;
+    int srow = wave * kSRows + (lane_t % kSRows);
+    if (srow >= rh) srow = rh - 1;
     const uint32_t offS = (uint32_t)(srow * 4);
 
     auto issue = [&](int kb, int stage) {
@@ -346,9 +370,9 @@ gemm_fp8_contig_kernel(int G, int64_t M, int64_t N, int64_t K, const uint8_t* __
       else wait_vmcnt<0>();
       block_barrier();
       if (kb + 3 < nkb) issue(kb + 3, ST);
-      // unconditional (the last step's reads are unused but in bounds): the reads and
-      // the MFMAs stay in one basic block, interleaved in a fixed order
-      mma_and_read(cur, sb_cur, std::integral_constant<int, (ST + 1) % kStages>{}, nxt);
+      // unconditional for busy waves (the last step's reads are unused but in bounds):
+      // the reads and the MFMAs stay in one basic block, interleaved in a fixed order
+      if (busy) mma_and_read(cur, sb_cur, std::integral_constant<int, (ST + 1) % kStages>{}, nxt);
       sb_cur = sbl_w[kb + 1 < nkb ? kb + 1 : kb];      // read now, waited at the next step's top
     };
 
@@ -373,7 +397,7 @@ gemm_fp8_contig_kernel(int G, int64_t M, int64_t N, int64_t K, const uint8_t* __
     else wait_vmcnt<0>();
     block_barrier();
     Frags f0, f1;
-    load_frags(std::integral_constant<int, 0>{}, f0);
+    if (busy) load_frags(std::integral_constant<int, 0>{}, f0);
     sb_cur = sbl_w[0];
 
     using I0 = std::integral_constant<int, 0>;
@@ -394,19 +418,21 @@ gemm_fp8_contig_kernel(int G, int64_t M, int64_t N, int64_t K, const uint8_t* __
       // maximum, s = max / 448 and the e4m3 codes (the rule of the 1x128 quantizer).
       constexpr int kRowF = 260;                   // floats per staged row (1040 bytes)
       float* stage = reinterpret_cast<float*>(smem);
+      const int lane_e = opaque(lane);
       __builtin_amdgcn_s_waitcnt(kLgkmZero);
       block_barrier();                             // every wave is done with the K loop's LDS
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < kNFrag; ++j)
-          *reinterpret_cast<v4f*>(stage + (wm * 64 + 16 * i + l16) * kRowF + wn * kWaveCols + 16 * j + 4 * q) =
+          *reinterpret_cast<v4f*>(stage + (wm * 64 + 16 * i + (lane_e & 15)) * kRowF + wn * kWaveCols + 16 * j +
+                                  4 * (lane_e >> 4)) =
               acc[i][j];
       __syncthreads();
       const int64_t I = N / 2;
-      for (int item = tid; item < BM * 16; item += kThreads) {
+      for (int item = opaque(tid); item < BM * 16; item += kThreads) {
         const int r = item >> 4, t16 = item & 15;
-        const bool live = r < rows_here;
+        const bool live = r < rows_valid;
         float a[8];
         const float* gp = stage + r * kRowF + 8 * t16;
 #pragma unroll
@@ -430,12 +456,14 @@ gemm_fp8_contig_kernel(int G, int64_t M, int64_t N, int64_t K, const uint8_t* __
       continue;                                    // the next tile starts with a barrier
     }
     // epilogue: lane holds columns n0 + wn*64 + 16j + 4q + (0..3) of row m0 + wm*64 + 16i + l16
-    if (wn * kWaveCols >= cols_here) continue;
+    if (wn * kWaveCols >= cols_here || !busy) continue;
+    const int lane_e = opaque(lane);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int64_t row = m0 + wm * 64 + 16 * i + l16;
-      if (row >= m_end) continue;
-      uint16_t* drow = D + row * ldd + n0 + wn * kWaveCols + 4 * q;
+      const int r = wm * 64 + 16 * i + (lane_e & 15);
+      if (r >= rows_valid) continue;
+      const int64_t row = m0 + r;
+      uint16_t* drow = D + row * ldd + n0 + wn * kWaveCols + 4 * (lane_e >> 4);
 #pragma unroll
       for (int j = 0; j < kNFrag; ++j) {
         const uint32_t lo = (uint32_t)bf16_bits_rne(acc[i][j][0]) | ((uint32_t)bf16_bits_rne(acc[i][j][1]) << 16);
@@ -654,8 +682,8 @@ gemm_fp8_dense_kernel(int64_t M, int64_t N, int64_t K, const uint8_t* __restrict
 
 hipError_t launch_gemm_fp8_contig(int32_t G, int64_t M, int64_t N, int64_t K, const uint8_t* a,
                                   const float* sa, const uint8_t* b, const float* sb,
-                                  const int32_t* offsets, uint16_t* d, int64_t ldd, int num_cus,
-                                  hipStream_t st) {
+                                  const int32_t* offsets, const int32_t* valid, uint16_t* d, int64_t ldd,
+                                  int num_cus, hipStream_t st) {
   if (M == 0 || N == 0) return hipSuccess;
   if (N % 128 != 0 || K % BK != 0) return hipErrorInvalidValue;
   if (offsets == nullptr && G == 1 && K / BK <= dense::kMaxKb) {
@@ -672,21 +700,21 @@ hipError_t launch_gemm_fp8_contig(int32_t G, int64_t M, int64_t N, int64_t K, co
   grid = (grid / kXcds) * kXcds;
   if (grid < kXcds * kSM) grid = kXcds * kSM;
   hipLaunchKernelGGL(gemm_fp8_contig_kernel<false>, dim3((unsigned)grid), dim3(kThreads), 0, st, G, M, N, K, a,
-                     sa, b, sb, offsets, d, ldd, nullptr, nullptr);
+                     sa, b, sb, offsets, valid, d, ldd, nullptr, nullptr);
   return hipGetLastError();
 }
 
 hipError_t launch_gemm_fp8_silu_quantize(int32_t G, int64_t M, int64_t I, int64_t K, const uint8_t* a,
                                          const float* sa, const uint8_t* b, const float* sb,
-                                         const int32_t* offsets, uint8_t* q, float* s, int num_cus,
-                                         hipStream_t st) {
+                                         const int32_t* offsets, const int32_t* valid, uint8_t* q, float* s,
+                                         int num_cus, hipStream_t st) {
   if (M == 0 || I == 0) return hipSuccess;
   if (I % 128 != 0 || K % BK != 0 || K / BK > kMaxKb) return hipErrorInvalidValue;
   int64_t grid = (int64_t)num_cus;
   grid = (grid / kXcds) * kXcds;
   if (grid < kXcds * kSM) grid = kXcds * kSM;
   hipLaunchKernelGGL(gemm_fp8_contig_kernel<true>, dim3((unsigned)grid), dim3(kThreads), 0, st, G, M, 2 * I, K, a,
-                     sa, b, sb, offsets, nullptr, (int64_t)0, q, s);
+                     sa, b, sb, offsets, valid, nullptr, (int64_t)0, q, s);
   return hipGetLastError();
 }
 

@@ -192,7 +192,12 @@ fgg_status fgg_moe_permute_quantize(const int32_t* topk_ids, int64_t T, int32_t 
  *   expert g; M is the row count of A, sA and D (e.g. M_cap of the permute);
  *   every offsets[g] must be a multiple of 128 (moe_permute with align 128
  *   guarantees it) and offsets[G] <= M.  Rows >= offsets[G] are not read
- *   or written.  aq = {E4M3,F32,1,128}: a [M][K], a_scales [K/128][M];
+ *   or written.  masked_m is optional here (NULL: every row of a segment is
+ *   computed); when given, masked_m[g] (clamped to [0, segment length]) is
+ *   group g's number of real rows, e.g. the permute's counts, and the rows
+ *   [offsets[g] + masked_m[g], offsets[g+1]) are padding: not written, and
+ *   their MFMA work is skipped in 64-row units (their A rows may still be
+ *   read).  aq = {E4M3,F32,1,128}: a [M][K], a_scales [K/128][M];
  *   bq = {E4M3,F32,128,128}: b [G][N][K], b_scales [G][N/128][K/128].
  * FGG_LAYOUT_MASKED (decode): A is [G][M][K] (M = rows per group, <= 16);
  *   group g uses rows m < masked_m[g] (values clamped to [0, M]); other rows
@@ -226,7 +231,9 @@ fgg_status fgg_grouped_gemm_scaled(fgg_layout layout, int32_t G, int64_t M, int6
  *   q_out[r][c], s_out[c/128][r] = the 1x128 e4m3 quantization of a (the rule of
  *   fgg_quantize_blockwise: s = max|a| / 448 per 128 columns, codes = RNE(a / s))
  * q_out is [M][I] bytes, s_out [I/128][M] fp32 (K-block-major, the activation
- * layout of the down GEMM).  Rows >= offsets[G] are not written.  The
+ * layout of the down GEMM).  Rows >= offsets[G] are not written.  counts
+ * (optional, [G] int32) has the meaning of masked_m in fgg_grouped_gemm_scaled
+ * CONTIGUOUS: padding rows past offsets[g] + counts[g] are not written.  The
  * separate path (bf16 H from fgg_grouped_gemm_scaled, then
  * fgg_quantize_blockwise with FGG_ACT_SILU_MUL) rounds H to bf16 first, so the
  * two may differ by one code where a value sits at a rounding boundary.
@@ -234,8 +241,8 @@ fgg_status fgg_grouped_gemm_scaled(fgg_layout layout, int32_t G, int64_t M, int6
  */
 fgg_status fgg_grouped_gemm_silu_quantize(int32_t G, int64_t M, int64_t I, int64_t K, const void* a,
                                           const void* a_scales, fgg_qdesc aq, const void* b, const void* b_scales,
-                                          fgg_qdesc bq, const int32_t* offsets, void* q_out, float* s_out,
-                                          void* stream);
+                                          fgg_qdesc bq, const int32_t* offsets, const int32_t* counts,
+                                          void* q_out, float* s_out, void* stream);
 
 /*
  * fgg_scaled_gemm — the dense one-group case ([MegaMoE] §2.1 fp8_gemm with

@@ -116,9 +116,9 @@ def test_gemm_and_permute_reject_bad_arguments_on_host():
     assert Q(g, 10, 2, 2000, 128, g, fgg.FGG_BF16, 256, 256, g, g, g, g, g, g, 100, g, 1 << 20, None) == 1
     # fused gate-up + SiLU requant: I not a multiple of 128, FP4 weights, missing offsets
     F = lib.fgg_grouped_gemm_silu_quantize
-    assert F(2, 256, 100, 256, g, g, A, g, g, B8, g, g, g, None) == 2
-    assert F(2, 256, 128, 256, g, g, A, g, g, B4, g, g, g, None) == 2
-    assert F(2, 256, 128, 256, g, g, A, g, g, B8, None, g, g, None) == 1
-    assert F(0, 256, 128, 256, g, g, A, g, g, B8, g, g, g, None) == 1
+    assert F(2, 256, 100, 256, g, g, A, g, g, B8, g, None, g, g, None) == 2
+    assert F(2, 256, 128, 256, g, g, A, g, g, B4, g, None, g, g, None) == 2
+    assert F(2, 256, 128, 256, g, g, A, g, g, B8, None, None, g, g, None) == 1
+    assert F(0, 256, 128, 256, g, g, A, g, g, B8, g, None, g, g, None) == 1
     # combine: N not a multiple of 8
     assert lib.fgg_moe_combine(g, 16, g, g, 4, 2, 12, g, 16, None) == 2

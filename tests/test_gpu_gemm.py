@@ -118,6 +118,38 @@ def test_grouped_contiguous_small(counts, N, K):
     assert np.all(np.isnan(y[mt:]))                            # rows >= offsets[G] untouched
 
 
+def _valid_rows(offsets, masked):
+    """Rows [offsets[e], offsets[e] + clamp(masked[e], 0, segment length)) per group."""
+    rows = []
+    for e in range(len(masked)):
+        n = min(max(int(masked[e]), 0), int(offsets[e + 1] - offsets[e]))
+        rows.extend(range(int(offsets[e]), int(offsets[e]) + n))
+    return np.array(rows, np.int64)
+
+
+@pytest.mark.parametrize("counts,masked,N,K", [
+    ([5, 0, 300, 128], [5, 0, 300, 128], 256, 512),        # tiles with 5 and 44 real rows
+    ([5, 0, 300, 128], [2000, 7, -3, 64], 256, 512),       # clamped above / below, half tile
+    ([129, 1000], [129, 1000], 384, 1024),
+    ([64, 65], [64, 65], 128, 256)])                       # exactly one busy row half, and one more row
+def test_grouped_contiguous_valid_counts(counts, masked, N, K):
+    """Per-group real row counts (masked_m with the contiguous layout): the rows
+    they cover equal the unmasked call bit for bit; padding rows past them are
+    not written."""
+    x, w, offsets = _contig_case(len(counts) * 37 + N, counts, N, K)
+    xq, xs = fgg.quantize_blockwise(cuda(x), fgg.Q_E4M3_1x128)
+    bq, sb = _quant_weights_gpu(w, fgg.Q_E4M3_128x128)
+    full = to_np(fgg.grouped_gemm_scaled(xq, xs, bq, sb, offsets=cuda(offsets)))
+    d = torch.full((x.shape[0], N), float("nan"), dtype=torch.bfloat16, device="cuda")
+    fgg.grouped_gemm_scaled(xq, xs, bq, sb, offsets=cuda(offsets), masked_m=cuda(np.array(masked, np.int32)),
+                            out=d)
+    y = to_np(d)
+    rows = _valid_rows(offsets, masked)
+    assert np.array_equal(y[rows], full[rows])
+    rest = np.setdiff1d(np.arange(x.shape[0]), rows)
+    assert np.all(np.isnan(y[rest]))
+
+
 @pytest.mark.parametrize("M,N,K", [(500, 256, 1024), (128, 128, 128), (1, 128, 256)])
 def test_dense_small_and_one_group_identity(M, N, K):
     g = synth.rng(M + N + K)
@@ -156,15 +188,18 @@ def test_dense_full_size_sampled_and_deterministic():
 
 # ------------------------------------------------------------- MoE chains
 
-def _moe_chain_gpu(x, topk_ids, topk_w, E, wq_gu, ws_gu, wq_dn=None, ws_dn=None):
+def _moe_chain_gpu(x, topk_ids, topk_w, E, wq_gu, ws_gu, wq_dn=None, ws_dn=None, use_counts=False):
+    """use_counts: both GEMMs get the permute's counts, so padding rows are skipped
+    (and their outputs left unwritten)."""
     xq, xs = fgg.quantize_blockwise(cuda(x), fgg.Q_E4M3_1x128)
     perm = fgg.moe_permute(cuda(topk_ids), E, 128, xq=xq, xs=xs)
-    h = fgg.grouped_gemm_scaled(perm["a"], perm["sa"], wq_gu, ws_gu, offsets=perm["offsets"])
+    mm = perm["counts"] if use_counts else None
+    h = fgg.grouped_gemm_scaled(perm["a"], perm["sa"], wq_gu, ws_gu, offsets=perm["offsets"], masked_m=mm)
     if wq_dn is None:
         y = h
     else:
         a2, s2 = fgg.quantize_blockwise(h, fgg.Q_E4M3_1x128, silu_mul=True)
-        y = fgg.grouped_gemm_scaled(a2, s2, wq_dn, ws_dn, offsets=perm["offsets"])
+        y = fgg.grouped_gemm_scaled(a2, s2, wq_dn, ws_dn, offsets=perm["offsets"], masked_m=mm)
     out = fgg.moe_combine(y, perm["src_to_row"], cuda(topk_w))
     return out, perm, h, y
 
@@ -237,6 +272,11 @@ def test_moe_prefill_full_size_sampled():
         y_ref = oracle.round_bf16(oracle.grouped_gemm_contiguous(
             a2_r, s2_r, bq2[None], sb2[None], np.array([0, len(rows)])))
         tol_check(to_np(y)[rows], y_ref, what=f"prefill down expert {e}")
+    # the same chain with the permute's counts given to both GEMMs: padding rows are
+    # skipped, and the combined output is identical bit for bit
+    out_c, _, _, _ = _moe_chain_gpu(x, r["topk_ids"], r["topk_w"], E, gu_q, gu_s, dn_q, dn_s, use_counts=True)
+    assert torch.equal(out_c, out)
+    del out_c
     # combine for a sample of tokens, from the GPU's own expert outputs
     toks = np.arange(0, T, 997)
     y_np = to_np(y)
@@ -430,6 +470,27 @@ def test_grouped_silu_quantize_small(counts, I, K):
         assert np.all(q[lo:hi] == 0) and np.all(s[:, lo:hi] == 1.0)
 
 
+@pytest.mark.parametrize("counts,masked,I,K", [([5, 0, 300, 128], [5, 0, 300, 128], 128, 512),
+                                               ([5, 0, 300, 128], [2000, 7, -3, 64], 256, 512)])
+def test_grouped_silu_quantize_valid_counts(counts, masked, I, K):
+    """Per-group real row counts: the rows they cover equal the call without
+    counts bit for bit; codes and scales of padding rows are not written."""
+    x, w, offsets = _contig_case(len(counts) * 19 + I + K, counts, 2 * I, K)
+    xq, xs = fgg.quantize_blockwise(cuda(x), fgg.Q_E4M3_1x128)
+    bq, sb = _quant_weights_gpu(w, fgg.Q_E4M3_128x128)
+    M = x.shape[0]
+    q0, s0 = fgg.grouped_gemm_silu_quantize(xq, xs, bq, sb, cuda(offsets))
+    q = torch.full((M, I), 0xAB, dtype=torch.uint8, device="cuda")
+    s = torch.full((I // 128, M), -3.0, dtype=torch.float32, device="cuda")
+    fgg.grouped_gemm_silu_quantize(xq, xs, bq, sb, cuda(offsets), counts=cuda(np.array(masked, np.int32)),
+                                   out=q, scales=s)
+    q, s, q0, s0 = to_np(q), to_np(s), to_np(q0), to_np(s0)
+    rows = _valid_rows(offsets, masked)
+    assert np.array_equal(q[rows], q0[rows]) and np.array_equal(s[:, rows], s0[:, rows])
+    rest = np.setdiff1d(np.arange(M), rows)
+    assert np.all(q[rest] == 0xAB) and np.all(s[:, rest] == -3.0)
+
+
 def test_grouped_silu_quantize_prefill_matches_separate_path():
     """Full prefill gate-up shape: the fused kernel against the separate GEMM +
     SiLU requant (bf16 H in between), and sampled rows against the oracle."""
@@ -449,6 +510,11 @@ def test_grouped_silu_quantize_prefill_matches_separate_path():
     gu_q, gu_s = torch.stack(gu_q), torch.stack(gu_s)
     offs = perm["offsets"]
     q, s = fgg.grouped_gemm_silu_quantize(perm["a"], perm["sa"], gu_q, gu_s, offs)
+    # with the permute's counts (padding rows skipped): identical on the real rows
+    qc, sc = fgg.grouped_gemm_silu_quantize(perm["a"], perm["sa"], gu_q, gu_s, offs, counts=perm["counts"])
+    real = _valid_rows(to_np(offs), to_np(perm["counts"]))
+    assert np.array_equal(to_np(qc)[real], to_np(q)[real]) and np.array_equal(to_np(sc)[:, real], to_np(s)[:, real])
+    del qc, sc
     h = fgg.grouped_gemm_scaled(perm["a"], perm["sa"], gu_q, gu_s, offsets=offs)
     q2, s2 = fgg.quantize_blockwise(h, fgg.Q_E4M3_1x128, silu_mul=True, rows_dev=offs[E:])
     mt = int(to_np(offs)[E])
