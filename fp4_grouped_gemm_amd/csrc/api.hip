@@ -180,7 +180,8 @@ fgg_status fgg_grouped_gemm_scaled(fgg_layout layout, int32_t G, int64_t M, int6
   if (N % 128 != 0 || K % 128 != 0) return FGG_ERR_UNSUPPORTED;
   if (ldd < N || ldd % 8 != 0) return FGG_ERR_INVALID_VALUE;
   if (!same_q(aq, FGG_E4M3, FGG_F32, 1, 128)) return FGG_ERR_UNSUPPORTED;
-  if (!a || !a_scales || !b || !b_scales || !d) return FGG_ERR_INVALID_VALUE;
+  // (with K == 0 the operands hold no bytes and are never read: they may be NULL)
+  if ((K > 0 && (!a || !a_scales || !b || !b_scales)) || !d) return FGG_ERR_INVALID_VALUE;
   if (!aligned(a, 16) || !aligned(b, 16) || !aligned(d, 16) || !aligned(a_scales, 4) || !aligned(b_scales, 4))
     return FGG_ERR_INVALID_VALUE;
   int num_cus = 0;
@@ -201,7 +202,7 @@ fgg_status fgg_grouped_gemm_scaled(fgg_layout layout, int32_t G, int64_t M, int6
   if (layout == FGG_LAYOUT_MASKED) {
     const bool fp4 = same_q(bq, FGG_E2M1X2, FGG_E8M0, 1, 32);
     if (!fp4 && !same_q(bq, FGG_E4M3, FGG_F32, 128, 128)) return FGG_ERR_UNSUPPORTED;
-    if (M > 16) return FGG_ERR_UNSUPPORTED;
+    if (M > 16 || K == 0) return FGG_ERR_UNSUPPORTED;
     if (!masked_m) return FGG_ERR_INVALID_VALUE;
     fgg_status st = device_check(&num_cus);
     if (st != FGG_OK) return st;
@@ -220,7 +221,7 @@ fgg_status fgg_grouped_gemm_silu_quantize(int32_t G, int64_t M, int64_t I, int64
   if (G < 1 || G > 1024 || M < 0 || I < 0 || K < 0) return FGG_ERR_INVALID_VALUE;
   if (I % 128 != 0 || K % 128 != 0 || K > 16384) return FGG_ERR_UNSUPPORTED;
   if (!same_q(aq, FGG_E4M3, FGG_F32, 1, 128) || !same_q(bq, FGG_E4M3, FGG_F32, 128, 128)) return FGG_ERR_UNSUPPORTED;
-  if (!a || !a_scales || !b || !b_scales || !offsets || !q_out || !s_out) return FGG_ERR_INVALID_VALUE;
+  if ((K > 0 && (!a || !a_scales || !b || !b_scales)) || !offsets || !q_out || !s_out) return FGG_ERR_INVALID_VALUE;
   if (!aligned(a, 16) || !aligned(b, 16) || !aligned(q_out, 16) || !aligned(a_scales, 4) || !aligned(b_scales, 4) ||
       !aligned(s_out, 4))
     return FGG_ERR_INVALID_VALUE;
@@ -250,7 +251,8 @@ fgg_status fgg_scaled_gemm(int64_t M, int64_t N, int64_t K, const void* a, const
   if (M < 0 || N < 0 || K < 0) return FGG_ERR_INVALID_VALUE;
   if (N % 128 != 0 || K % 128 != 0) return FGG_ERR_UNSUPPORTED;
   if (ldd < N || ldd % 8 != 0) return FGG_ERR_INVALID_VALUE;
-  if (!a || !a_scales || !b || !b_scales || !d) return FGG_ERR_INVALID_VALUE;
+  // (with K == 0 the operands hold no bytes and are never read: they may be NULL)
+  if ((K > 0 && (!a || !a_scales || !b || !b_scales)) || !d) return FGG_ERR_INVALID_VALUE;
   if (!aligned(a, 16) || !aligned(b, 16) || !aligned(d, 16) || !aligned(a_scales, 4) || !aligned(b_scales, 4))
     return FGG_ERR_INVALID_VALUE;
   int num_cus = 0;
@@ -265,7 +267,7 @@ fgg_status fgg_scaled_gemm(int64_t M, int64_t N, int64_t K, const void* a, const
                                               (uint16_t*)d, ldd, num_cus, (hipStream_t)stream));
   }
   if (same_q(aq, FGG_E2M1X2, FGG_F32, 1, 16) && same_q(bq, FGG_E2M1X2, FGG_F32, 1, 16)) {
-    if (M % 128 != 0) return FGG_ERR_UNSUPPORTED;
+    if (M % 128 != 0 || K == 0) return FGG_ERR_UNSUPPORTED;
     if (!aligned(a_scales, 8) || !aligned(b_scales, 8)) return FGG_ERR_INVALID_VALUE;
     const int32_t rank = epi ? epi->rank : 0;
     if (rank != 0 && rank != 32) return FGG_ERR_UNSUPPORTED;

@@ -70,13 +70,20 @@ constexpr int kSBytes = BM * 4;                  // 512 B of activation scales
 constexpr int kAOff = 0;
 constexpr int kSOff = kStages * kABytes;
 constexpr int kBOff = kSOff + kStages * kSBytes;
-constexpr int kMaxKb = 128;                      // K <= 16384: the tile's weight scales fit one LDS slab
-constexpr int kSBOff = kBOff + kStages * kBBytes;  // [2 column blocks][kMaxKb] fp32 weight scales
-constexpr int kLdsBytes = kSBOff + 2 * kMaxKb * 4;
+constexpr int kMaxKb = 128;                      // K <= 16384 (the grouped entry points' limit)
+constexpr int kSBOff = kBOff + kStages * kBBytes;  // per stage: the weight scales of the two 128-column blocks
+constexpr int kSBStage = 16;
+constexpr int kMaxG = 1024;
+// per workgroup: offsets[0..G] and each group's end of real rows (offsets[g] + count)
+constexpr int kGrpOff = kSBOff + kStages * kSBStage;
+// SILU epilogue: per-row partial maxima of the 4 column waves, [2 row halves][4][64]
+constexpr int kRedOff = kGrpOff + (2 * kMaxG + 1) * 4;
+constexpr int kLdsBytes = kRedOff + 2 * 4 * 64 * 4;
 constexpr int kADma = kABytes / 1024 / kWaves;   // 16-byte-per-lane DMA instructions per wave
 constexpr int kBDma = kBBytes / 1024 / kWaves;
 constexpr int kSRows = BM / kWaves;              // activation scales per wave (dword DMA lanes)
-constexpr int kDmaPerStage = kADma + kBDma + 1;
+constexpr int kDmaPerStage = kADma + kBDma + 1;  // wave 0 issues one more: the stage's weight scales
+static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
 
 // 16-byte chunk swizzle of a 128-byte LDS row: rows r and r + 16 share a key, so
 // the operand fragments of one lane (rows 16 apart) sit at one base address plus
@@ -120,6 +127,16 @@ __device__ inline void wait_vmcnt() {
 
 __device__ inline void block_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
+// A pointer the compiler is told is the same in every lane (it is: built from
+// workgroup-uniform values), so that it can be a DMA instruction's scalar base.
+template <class T>
+__device__ inline T* uniform_ptr(T* p) {
+  const uint64_t v = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (T*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+
 // The value of x, hidden from the optimizer: address arithmetic derived from it is
 // computed where it is used (in a tile's epilogue) instead of being hoisted out of
 // the tile loop and held, or spilled, across the K loop.
@@ -128,16 +145,22 @@ __device__ inline int opaque(int x) {
   return x;
 }
 
-__device__ inline int find_group(const int32_t* __restrict__ offsets, int G, int64_t row) {
-  int lo = 0, hi = G - 1;           // largest g with offsets[g] <= row
+// largest g with offsets[g] <= row, by binary search over the workgroup's LDS copy of
+// the offsets (uniform: every lane reads the same entries)
+__device__ inline int find_group(const int32_t* offs, int G, int64_t row) {
+  int lo = 0, hi = G - 1;
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
-    if ((int64_t)offsets[mid] <= row) lo = mid; else hi = mid - 1;
+    const int v = __builtin_amdgcn_readfirstlane(offs[mid]);
+    if ((int64_t)v <= row) lo = mid; else hi = mid - 1;
   }
   return lo;
 }
 
 }  // namespace
+
+template <bool SILU>
+__device__ constexpr int bfrag_row(int j) { return SILU ? (j & 1) * 16 + (j >> 1) * 128 : 16 * j; }
 
 // SILU: the gate-up GEMM with SiLU(gate)·up and the 1x128 e4m3 requantization in the
 // epilogue.  B has N = 2I rows ([gate | up]); the tile of output block j (128
@@ -172,12 +195,31 @@ gemm_fp8_contig_kernel(int G, int64_t M, int64_t N, int64_t K, const uint8_t* __
 
   // Loop-invariant LDS read offsets (stage 0) of this lane's operand fragments:
   // fragment i is 16 rows (2048 bytes) further, stage s adds s * k{A,S,B}Bytes.
-  const int arow = wm * 64 + l16, brow = wn * kWaveCols + l16;
+  // B fragment rows: wave wn takes tile columns [64 wn, 64 wn + 64) as fragments j = 0..3,
+  // 16 rows apart; with SILU it takes gate columns [32 wn, 32 wn + 32) (fragments 0, 1,
+  // tile rows 32 wn + 16 j) and the up columns of the same indices (fragments 2, 3, tile
+  // rows 128 + 32 wn + 16 (j - 2)), so each lane holds matching gate and up outputs.
+  // Rows 16 and 128 apart share a swizzle key, so every fragment is the base plus an immediate.
+  const int arow = wm * 64 + l16, brow = (SILU ? 32 : kWaveCols) * wn + l16;
   const uint32_t ra_lo = kAOff + arow * BK + (((2 * q) ^ swz(arow)) << 4);
   const uint32_t ra_hi = kAOff + arow * BK + (((2 * q + 1) ^ swz(arow)) << 4);
   const uint32_t rb_lo = kBOff + brow * BK + (((2 * q) ^ swz(brow)) << 4);
   const uint32_t rb_hi = kBOff + brow * BK + (((2 * q + 1) ^ swz(brow)) << 4);
   const uint32_t rs = kSOff + arow * 4;
+
+  // The group table: every tile's expert search and row count come from LDS, so a tile
+  // starts without a chain of dependent global loads.
+  int32_t* grp = reinterpret_cast<int32_t*>(smem + kGrpOff);
+  if (offsets) {
+    for (int i = tid; i <= G; i += kThreads) grp[i] = offsets[i];
+    for (int i = tid; i < G; i += kThreads) {
+      const int s0 = offsets[i], len = offsets[i + 1] - s0;
+      int v = valid ? valid[i] : len;
+      v = v < 0 ? 0 : (v > len ? len : v);
+      grp[G + 1 + i] = s0 + v;
+    }
+  }
+  __syncthreads();
 
   // XCD-aware persistent schedule.  Workgroups are dispatched round-robin over
   // the 8 XCDs (workgroup b runs on XCD b % 8), each with its own L2.  The tile
@@ -189,48 +231,69 @@ gemm_fp8_contig_kernel(int G, int64_t M, int64_t N, int64_t K, const uint8_t* __
   const int sn_tiles = wg_per_xcd / kSM > 0 ? wg_per_xcd / kSM : 1;
   const int64_t st_m = (m_tiles + kSM - 1) / kSM, st_n = (n_tiles + sn_tiles - 1) / sn_tiles;
   const int64_t num_st = st_m * st_n;
-  for (int64_t st = xcd; st < num_st; st += kXcds) {
-    if (slot >= kSM * sn_tiles) break;
-    const int64_t mt = (st / st_n) * kSM + slot % kSM;
-    const int64_t nt = (st % st_n) * sn_tiles + slot / kSM;
-    if (mt >= m_tiles || nt >= n_tiles) continue;
-    const int64_t m0 = mt * BM, n0 = nt * BN;
-    const int g = offsets ? find_group(offsets, G, m0) : 0;
-    const int64_t rows_here = (m_end - m0) < BM ? (m_end - m0) : BM;   // >= 1
-    // rows of the tile that are computed and stored: with per-group valid counts, a
-    // segment's rows past offsets[g] + valid[g] are padding (neither computed nor stored)
-    int64_t rows_valid = rows_here;
-    if (valid != nullptr) {
-      const int64_t seg0 = offsets[g], seg_len = (int64_t)offsets[g + 1] - seg0;
-      int64_t v = valid[g];
-      v = v < 0 ? 0 : (v > seg_len ? seg_len : v);
-      if (seg0 + v - m0 < rows_valid) rows_valid = seg0 + v - m0;
-      if (rows_valid <= 0) continue;               // the whole tile is padding (uniform)
+
+  // The workgroup's tiles: one per super-tile xcd, xcd + 8, ...; tiles that hold only
+  // padding rows are skipped.
+  struct Tile {
+    int64_t st, m0, n0, nt;
+    int g, rows_here, rows_valid, cols_here;
+  };
+  auto find_tile = [&](int64_t from, Tile& t) -> bool {
+    if (slot >= kSM * sn_tiles) return false;
+    for (int64_t st = from; st < num_st; st += kXcds) {
+      const int64_t mt = (st / st_n) * kSM + slot % kSM;
+      const int64_t nt = (st % st_n) * sn_tiles + slot / kSM;
+      if (mt >= m_tiles || nt >= n_tiles) continue;
+      const int64_t m0 = mt * BM;
+      const int g = offsets ? find_group(grp, G, m0) : 0;
+      const int rows_here = (int)((m_end - m0) < BM ? (m_end - m0) : BM);   // >= 1
+      // rows that are computed and stored: with per-group valid counts, a segment's
+      // rows past offsets[g] + valid[g] are padding (neither computed nor stored)
+      int rows_valid = rows_here;
+      if (offsets) {
+        const int64_t vend = __builtin_amdgcn_readfirstlane(grp[G + 1 + g]);
+        if (vend - m0 < rows_valid) rows_valid = (int)(vend - m0);
+        if (rows_valid <= 0) continue;
+      }
+      t.st = st;
+      t.m0 = m0;
+      t.nt = nt;
+      t.n0 = nt * BN;
+      t.g = g;
+      t.rows_here = rows_here;
+      t.rows_valid = rows_valid;
+      t.cols_here = (int)((N - t.n0) < BN ? (N - t.n0) : BN);               // 128 or 256
+      return true;
     }
-    // a wave whose 64 rows are all padding only helps move data
-    const bool busy = wm * 64 < rows_valid;
-    const int64_t cols_here = (N - n0) < BN ? (N - n0) : BN;           // 128 or 256
-    const uint8_t* Atile = A + m0 * K;
+    return false;
+  };
+
+  // DMA state of the tile whose stages are being fetched.  Lane roles: lane l fills
+  // 16-byte LDS chunk (l % 8) of row (l / 8) of an 8-row group; it reads source chunk
+  // (l % 8) ^ swz(row), where swz(row) = (l / 8) ^ (row-group index & 1).  Rows past the
+  // end of A are redirected to the last valid row (their outputs are never stored).
+  // 32-bit arithmetic on lane values recomputed per tile (nothing hoisted or spilled).
+  const uint8_t* Atile = A;
+  const uint8_t* Btile = B;
+  const float* SAt = SA;
+  const float* SBg = SB;
+  uint32_t offA[kADma], offB[kBDma], offS = 0, offSB = 0;
+  auto set_dma = [&](const Tile& t) {
+    Atile = uniform_ptr(A + t.m0 * K);
     // this wave's B DMA rows are tile rows [32 * wave, 32 * wave + 32): with SILU, waves
     // 0-3 fetch gate rows and waves 4-7 up rows, each from its own base
-    const int64_t b_first = SILU ? (wave < 4 ? nt * 128 : N / 2 + nt * 128 - 128) : n0;
-    const uint8_t* Btile = B + ((int64_t)g * N + b_first) * K;
-
-    // DMA lane roles: lane l fills 16-byte LDS chunk (l % 8) of row (l / 8) of an 8-row group;
-    // it reads source chunk (l % 8) ^ swz(row), where swz(row) = (l / 8) ^ (row-group index & 1).
-    // Per-lane byte offsets (within the tile) of this wave's DMA rows; rows past the
-    // end of A are redirected to the last valid row (their outputs are never stored).
-    // 32-bit arithmetic on per-tile lane values (nothing hoisted, nothing spilled).
+    const int64_t b_first = SILU ? (wave < 4 ? t.nt * 128 : N / 2 + t.nt * 128 - 128) : t.n0;
+    Btile = uniform_ptr(B + ((int64_t)t.g * N + b_first) * K);
+    SAt = uniform_ptr(SA + t.m0);
+    SBg = uniform_ptr(SB + (int64_t)t.g * nblk * nkb);
     const int lane_t = opaque(lane);
     const int lrow = lane_t >> 3, lchunk = (lane_t & 7) ^ lrow;
-    const int rh = (int)rows_here, ch = (int)cols_here;
-    uint32_t offA[kADma], offB[kBDma];
 #pragma unroll
     for (int i = 0; i < kADma; ++i) {
       const int grp8 = wave * kADma + i;             // 8-row group of the A tile
       int row = grp8 * 8 + lrow;
       const int c = lchunk ^ (grp8 & 1);
-      if (row >= rh) row = rh - 1;
+      if (row >= t.rows_here) row = t.rows_here - 1;
       offA[i] = (uint32_t)row * (uint32_t)K + (uint32_t)(c * 16);
     }
 #pragma unroll
@@ -238,26 +301,53 @@ gemm_fp8_contig_kernel(int G, int64_t M, int64_t N, int64_t K, const uint8_t* __
       const int grp8 = wave * kBDma + i;
       int row = grp8 * 8 + lrow;
       const int c = lchunk ^ (grp8 & 1);
-      if (row >= ch) row = ch - 1;                   // half-wide last tile: stay inside B
+      if (row >= t.cols_here) row = t.cols_here - 1;   // half-wide last tile: stay inside B
       offB[i] = (uint32_t)row * (uint32_t)K + (uint32_t)(c * 16);
     }
     int srow = wave * kSRows + (lane_t % kSRows);
-    if (srow >= rh) srow = rh - 1;
-    const uint32_t offS = (uint32_t)(srow * 4);
+    if (srow >= t.rows_here) srow = t.rows_here - 1;
+    offS = (uint32_t)(srow * 4);
+    // weight scales: wave 0's lanes 0 and 1 fetch those of column halves 0 and 1 (with
+    // SILU: the gate block nt and the up block I/128 + nt) for each K block
+    int nbh = SILU ? (lane_t == 1 ? (int)(nblk / 2 + t.nt) : (int)t.nt) : (int)(t.n0 / 128) + (lane_t & 1);
+    if (nbh >= nblk) nbh = (int)nblk - 1;
+    offSB = (uint32_t)nbh * (uint32_t)nkb * 4u;
+  };
+  // K block kb of the DMA tile into LDS buffer `stage`
+  auto issue = [&](int kb, int stage) {
+    const uint8_t* a_src = Atile + (int64_t)kb * BK;
+    const uint8_t* b_src = Btile + (int64_t)kb * BK;
+#pragma unroll
+    for (int i = 0; i < kADma; ++i)
+      dma16(a_src, offA[i], lds_base + kAOff + stage * kABytes + (wave * kADma + i) * 1024);
+#pragma unroll
+    for (int i = 0; i < kBDma; ++i)
+      dma16(b_src, offB[i], lds_base + kBOff + stage * kBBytes + (wave * kBDma + i) * 1024);
+    // kSRows scales per wave: the first kSRows lanes only (still one DMA instruction per wave)
+    const float* s_src = SAt + (int64_t)kb * M;
+    if (lane < kSRows) dma4(s_src, offS, lds_base + kSOff + stage * kSBytes + wave * kSRows * 4);
+    if (wave == 0 && lane < 2) dma4(SBg + kb, offSB, lds_base + kSBOff + stage * kSBStage);
+  };
 
-    auto issue = [&](int kb, int stage) {
-      const uint8_t* a_src = Atile + (int64_t)kb * BK;
-      const uint8_t* b_src = Btile + (int64_t)kb * BK;
-#pragma unroll
-      for (int i = 0; i < kADma; ++i)
-        dma16(a_src, offA[i], lds_base + kAOff + stage * kABytes + (wave * kADma + i) * 1024);
-#pragma unroll
-      for (int i = 0; i < kBDma; ++i)
-        dma16(b_src, offB[i], lds_base + kBOff + stage * kBBytes + (wave * kBDma + i) * 1024);
-      // kSRows scales per wave: the first kSRows lanes only (still one DMA instruction per wave)
-      const float* s_src = SA + (int64_t)kb * M + m0;
-      if (lane < kSRows) dma4(s_src, offS, lds_base + kSOff + stage * kSBytes + wave * kSRows * 4);
-    };
+  // this wave's weight scales: its 64 columns lie in column half (wn * 64) / 128; with
+  // SILU, fragments 0, 1 use the gate block's (half 0) and fragments 2, 3 the up block's
+  const float* sbl_w = reinterpret_cast<const float*>(smem + kSBOff) + (SILU ? 0 : (wn * kWaveCols) / 128);
+
+  Tile cur;
+  if (!find_tile(xcd, cur)) return;
+  set_dma(cur);
+  // The weight scales travel with each stage's DMA (into LDS), so the K loop issues
+  // no scalar loads: those share lgkmcnt with the LDS fragment reads and would force
+  // a full drain before every promotion.
+  if (nkb > 0) issue(0, 0);                        // (K == 0: no stages; the outputs are zeros)
+  if (nkb > 1) issue(1, 1);
+  if (nkb > 2) issue(2, 2);
+
+  while (true) {
+    Tile nxt;
+    const bool have_next = find_tile(cur.st + kXcds, nxt);
+    // a wave whose 64 rows are all padding only helps move data
+    const bool busy = wm * 64 < cur.rows_valid;
 
     v4f acc[4][kNFrag];
 #pragma unroll
@@ -283,8 +373,8 @@ gemm_fp8_contig_kernel(int G, int64_t M, int64_t N, int64_t K, const uint8_t* __
       }
 #pragma unroll
       for (int j = 0; j < kNFrag; ++j) {
-        const uint4 lo = *reinterpret_cast<const uint4*>(smem + rb_lo + ST * kBBytes + j * 16 * BK);
-        const uint4 hi = *reinterpret_cast<const uint4*>(smem + rb_hi + ST * kBBytes + j * 16 * BK);
+        const uint4 lo = *reinterpret_cast<const uint4*>(smem + rb_lo + ST * kBBytes + bfrag_row<SILU>(j) * BK);
+        const uint4 hi = *reinterpret_cast<const uint4*>(smem + rb_hi + ST * kBBytes + bfrag_row<SILU>(j) * BK);
         f.b[j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
       }
     };
@@ -295,11 +385,14 @@ gemm_fp8_contig_kernel(int G, int64_t M, int64_t N, int64_t K, const uint8_t* __
     // The promotion therefore trails its MFMA by two MFMA issues (three result
     // registers in rotation), so the matrix core never waits for the vector ALU
     // and no FMA waits for a result still in flight.
-    auto mma_and_read = [&](const Frags& f, float sb, auto nst_tag, Frags& nxt) {
+    auto mma_and_read = [&](const Frags& f, const float (&sb)[2], auto nst_tag, Frags& nxt) {
       constexpr int NST = decltype(nst_tag)::value;
-      float sab[4];
+      constexpr int NH = SILU ? 2 : 1;              // weight-scale blocks per wave
+      float sab[NH][4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sab[i] = f.s[i] * sb;
+      for (int h = 0; h < NH; ++h)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sab[h][i] = f.s[i] * sb[h];
       constexpr int T = 4 * kNFrag;
       v4f p[3];
       uint4 rd[20];
@@ -314,7 +407,7 @@ gemm_fp8_contig_kernel(int G, int64_t M, int64_t N, int64_t K, const uint8_t* __
           nxt.s[i] = *reinterpret_cast<const float*>(smem + rs + NST * kSBytes + i * 16 * 4);
         } else {
           const int j = (r - 12) >> 1;
-          const uint32_t off = ((r & 1) ? rb_hi : rb_lo) + NST * kBBytes + j * 16 * BK;
+          const uint32_t off = ((r & 1) ? rb_hi : rb_lo) + NST * kBBytes + bfrag_row<SILU>(j) * BK;
           rd[r] = *reinterpret_cast<const uint4*>(smem + off);
         }
       };
@@ -333,7 +426,7 @@ gemm_fp8_contig_kernel(int G, int64_t M, int64_t N, int64_t K, const uint8_t* __
           const int u = t - 2;
           const v4f& r = p[u % 3];
           v4f& c = acc[u / kNFrag][u % kNFrag];
-          const float sc = sab[u / kNFrag];
+          const float sc = sab[SILU ? (u % kNFrag) >> 1 : 0][u / kNFrag];
           c[0] = fmaf(r[0], sc, c[0]);
           c[1] = fmaf(r[1], sc, c[1]);
           c[2] = fmaf(r[2], sc, c[2]);
@@ -359,46 +452,40 @@ gemm_fp8_contig_kernel(int G, int64_t M, int64_t N, int64_t K, const uint8_t* __
     // registers and the fragments of stage kb + 1 are read from LDS.
     //   top of step kb: this wave's DMA of stage kb + 1 done (stage kb + 2 may fly),
     //   its LDS reads of stage kb done; barrier -> true for all waves.
-    const float* sbl_w = reinterpret_cast<const float*>(smem + kSBOff) + ((wn * kWaveCols) / 128) * kMaxKb;
-    float sb_cur = 0.f;
-    auto step = [&](auto st_tag, Frags& cur, Frags& nxt, int kb) {
+    float sb_cur[2] = {0.f, 0.f};
+    auto read_sb = [&](int slot) {
+      sb_cur[0] = sbl_w[slot * (kSBStage / 4)];
+      if constexpr (SILU) sb_cur[1] = sbl_w[slot * (kSBStage / 4) + 1];
+    };
+    auto step = [&](auto st_tag, Frags& cf, Frags& nf, int kb) {
       constexpr int ST = decltype(st_tag)::value;       // == kb % 3
       // all of this wave's LDS reads (the fragments of stage kb, the scale) are done:
       // a real s_waitcnt the compiler sees, so it needs no wait inside the MFMA run
       __builtin_amdgcn_s_waitcnt(kLgkmZero);
-      if (kb + 2 < nkb) wait_vmcnt<kDmaPerStage>();
-      else wait_vmcnt<0>();
+      if (kb + 2 < nkb) {
+        if (wave == 0) wait_vmcnt<kDmaPerStage + 1>();
+        else wait_vmcnt<kDmaPerStage>();
+      } else {
+        wait_vmcnt<0>();
+      }
       block_barrier();
       if (kb + 3 < nkb) issue(kb + 3, ST);
       // unconditional for busy waves (the last step's reads are unused but in bounds):
       // the reads and the MFMAs stay in one basic block, interleaved in a fixed order
-      if (busy) mma_and_read(cur, sb_cur, std::integral_constant<int, (ST + 1) % kStages>{}, nxt);
-      sb_cur = sbl_w[kb + 1 < nkb ? kb + 1 : kb];      // read now, waited at the next step's top
+      if (busy) mma_and_read(cf, sb_cur, std::integral_constant<int, (ST + 1) % kStages>{}, nf);
+      // stage kb + 1's weight scale (complete since this step's barrier), waited at the
+      // next step's top; after the last step the slot is stale and unused
+      read_sb((ST + 1) % kStages);
     };
 
-    block_barrier();          // every wave is done with the previous tile's LDS
-    // The tile's weight scales (one 128-column block per wave column pair, all K blocks)
-    // go to LDS once, so the K loop issues no scalar loads: those share lgkmcnt with
-    // the LDS fragment reads and would force a full drain before every promotion.
-    {
-      float* sbl = reinterpret_cast<float*>(smem + kSBOff);
-      for (int t = tid; t < 2 * nkb; t += kThreads) {
-        const int half = t / nkb, kb = t % nkb;
-        int64_t nbh = SILU ? (half ? nblk / 2 + nt : nt) : n0 / 128 + half;
-        if (nbh >= nblk) nbh = nblk - 1;
-        sbl[half * kMaxKb + kb] = SB[((int64_t)g * nblk + nbh) * nkb + kb];
-      }
-    }
-    issue(0, 0);
-    if (nkb > 1) issue(1, 1);
-    if (nkb > 2) issue(2, 2);
-    if (nkb > 2) wait_vmcnt<2 * kDmaPerStage>();
-    else if (nkb > 1) wait_vmcnt<kDmaPerStage>();
-    else wait_vmcnt<0>();
+    // The tile's first stages are in flight, and so may be the previous tile's output
+    // stores, which need not complete in order with the loads: wait for all of them.
+    wait_vmcnt<0>();
+    __builtin_amdgcn_s_waitcnt(kLgkmZero);
     block_barrier();
     Frags f0, f1;
     if (busy) load_frags(std::integral_constant<int, 0>{}, f0);
-    sb_cur = sbl_w[0];
+    read_sb(0);
 
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
@@ -412,64 +499,99 @@ gemm_fp8_contig_kernel(int G, int64_t M, int64_t N, int64_t K, const uint8_t* __
       if (kb + 5 < nkb) step(I2{}, f1, f0, kb + 5);
     }
 
+    // The next tile's first stages.  With SILU they are fetched now, behind the long
+    // (VALU-bound) epilogue: every wave's reads of the stages are done (the last step's
+    // barrier; that step's own reads are unused).  Without, the bf16 output stores go
+    // first and the stages after them (measured faster: the stores of all workgroups
+    // drain at once, and queued behind the stage loads they delay the next K loop).
+    constexpr bool kEarlyStages = SILU;
+    if (kEarlyStages && have_next) {
+      set_dma(nxt);
+      if (nkb > 0) issue(0, 0);
+      if (nkb > 1) issue(1, 1);
+      if (nkb > 2) issue(2, 2);
+    }
     if constexpr (SILU) {
-      // Stage the fp32 tile in LDS (rows padded to 1040 bytes), then 16 threads per
-      // row and 128-column group: a = SiLU(gate) * up on the fp32 values, the group
-      // maximum, s = max / 448 and the e4m3 codes (the rule of the 1x128 quantizer).
-      constexpr int kRowF = 260;                   // floats per staged row (1040 bytes)
-      float* stage = reinterpret_cast<float*>(smem);
+      // In registers: lane (l16, q) of wave (wm, wn) holds gate and up of activation
+      // columns 128 nt + 32 wn + 16 jj + 4 q + e (jj, e in 0..1, 0..3) for rows
+      // 64 wm + 16 i + l16.  a = SiLU(gate) * up in fp32; the row's maximum over the 128
+      // columns: over the lane's 8 values, the 4 lanes q (shuffles) and the 4 column
+      // waves (LDS); s = max / 448 and the e4m3 codes (the rule of the 1x128 quantizer).
       const int lane_e = opaque(lane);
+      const int le16 = lane_e & 15, qe = lane_e >> 4;
+      float amax[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        amax[i] = 0.0f;
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float gv = acc[i][jj][e];
+            const float a = div_by_ge1(gv, 1.0f + exp_neg(gv)) * acc[i][jj + 2][e];
+            acc[i][jj][e] = a;
+            amax[i] = fmaxf(amax[i], fabsf(a));
+          }
+        amax[i] = fmaxf(amax[i], __shfl_xor(amax[i], 16));
+        amax[i] = fmaxf(amax[i], __shfl_xor(amax[i], 32));
+      }
+      float* red = reinterpret_cast<float*>(smem + kRedOff);
+      if (qe == 0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) red[(wm * 4 + wn) * 64 + 16 * i + le16] = amax[i];
+      }
       __builtin_amdgcn_s_waitcnt(kLgkmZero);
-      block_barrier();                             // every wave is done with the K loop's LDS
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < kNFrag; ++j)
-          *reinterpret_cast<v4f*>(stage + (wm * 64 + 16 * i + (lane_e & 15)) * kRowF + wn * kWaveCols + 16 * j +
-                                  4 * (lane_e >> 4)) =
-              acc[i][j];
-      __syncthreads();
+      block_barrier();
       const int64_t I = N / 2;
-      for (int item = opaque(tid); item < BM * 16; item += kThreads) {
-        const int r = item >> 4, t16 = item & 15;
-        const bool live = r < rows_valid;
-        float a[8];
-        const float* gp = stage + r * kRowF + 8 * t16;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) a[e] = div_by_ge1(gp[e], 1.0f + exp_neg(gp[e])) * gp[128 + e];
-        float amax = 0.0f;
+      for (int i = 0; i < 4; ++i) {
+        const int r = wm * 64 + 16 * i + le16;
+        float m = red[(wm * 4) * 64 + 16 * i + le16];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(a[e]));
-        amax = group_max<16>(amax);
-        const float sc = (amax == 0.0f) ? 1.0f : amax / 448.0f;
+        for (int w = 1; w < 4; ++w) m = fmaxf(m, red[(wm * 4 + w) * 64 + 16 * i + le16]);
+        const float sc = (m == 0.0f) ? 1.0f : m / 448.0f;
         const float rc = __builtin_amdgcn_rcpf(sc);
-        float y[8];
+        if (r < cur.rows_valid) {
+          const int64_t row = cur.m0 + r;
+          uint8_t* qrow = Q + row * I + cur.nt * 128 + 32 * wn + 4 * qe;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) y[e] = e4m3_quotient(a[e], sc, rc);
-        if (live) {
-          const int64_t row = m0 + r;
-          *reinterpret_cast<uint2*>(Q + row * I + nt * 128 + 8 * t16) =
-              make_uint2(e4m3_pack4(y[0], y[1], y[2], y[3]), e4m3_pack4(y[4], y[5], y[6], y[7]));
-          if (t16 == 0) S[nt * M + row] = sc;
+          for (int jj = 0; jj < 2; ++jj) {
+            const v4f& a = acc[i][jj];
+            *reinterpret_cast<uint32_t*>(qrow + 16 * jj) =
+                e4m3_pack4(e4m3_quotient(a[0], sc, rc), e4m3_quotient(a[1], sc, rc), e4m3_quotient(a[2], sc, rc),
+                           e4m3_quotient(a[3], sc, rc));
+          }
+          if (wn == 0 && qe == 0) S[cur.nt * M + row] = sc;
         }
       }
-      continue;                                    // the next tile starts with a barrier
     }
     // epilogue: lane holds columns n0 + wn*64 + 16j + 4q + (0..3) of row m0 + wm*64 + 16i + l16
-    if (wn * kWaveCols >= cols_here || !busy) continue;
-    const int lane_e = opaque(lane);
+    if constexpr (!SILU) {
+      if (wn * kWaveCols < cur.cols_here && busy) {
+        const int lane_e = opaque(lane);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = wm * 64 + 16 * i + (lane_e & 15);
-      if (r >= rows_valid) continue;
-      const int64_t row = m0 + r;
-      uint16_t* drow = D + row * ldd + n0 + wn * kWaveCols + 4 * (lane_e >> 4);
+        for (int i = 0; i < 4; ++i) {
+          const int r = wm * 64 + 16 * i + (lane_e & 15);
+          if (r >= cur.rows_valid) continue;
+          const int64_t row = cur.m0 + r;
+          uint16_t* drow = D + row * ldd + cur.n0 + wn * kWaveCols + 4 * (lane_e >> 4);
 #pragma unroll
-      for (int j = 0; j < kNFrag; ++j) {
-        const uint32_t lo = (uint32_t)bf16_bits_rne(acc[i][j][0]) | ((uint32_t)bf16_bits_rne(acc[i][j][1]) << 16);
-        const uint32_t hi = (uint32_t)bf16_bits_rne(acc[i][j][2]) | ((uint32_t)bf16_bits_rne(acc[i][j][3]) << 16);
-        *reinterpret_cast<uint2*>(drow + 16 * j) = make_uint2(lo, hi);
+          for (int j = 0; j < kNFrag; ++j) {
+            const uint32_t lo = (uint32_t)bf16_bits_rne(acc[i][j][0]) | ((uint32_t)bf16_bits_rne(acc[i][j][1]) << 16);
+            const uint32_t hi = (uint32_t)bf16_bits_rne(acc[i][j][2]) | ((uint32_t)bf16_bits_rne(acc[i][j][3]) << 16);
+            *reinterpret_cast<uint2*>(drow + 16 * j) = make_uint2(lo, hi);
+          }
+        }
       }
+    }
+
+    if (!have_next) break;
+    cur = nxt;
+    if (!kEarlyStages) {
+      set_dma(cur);
+      if (nkb > 0) issue(0, 0);
+      if (nkb > 1) issue(1, 1);
+      if (nkb > 2) issue(2, 2);
     }
   }
 }
@@ -646,7 +768,7 @@ gemm_fp8_dense_kernel(int64_t M, int64_t N, int64_t K, const uint8_t* __restrict
         sbl[half * kMaxKb + kb] = SB[nbh * nkb + kb];
       }
     }
-    issue(0, 0);
+    if (nkb > 0) issue(0, 0);                      // (K == 0: the outputs are zeros)
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
     // top of step kb: this wave's DMA of stage kb done, then the barrier makes it true for
@@ -695,6 +817,7 @@ hipError_t launch_gemm_fp8_contig(int32_t G, int64_t M, int64_t N, int64_t K, co
                        b, sb, d, ldd);
     return hipGetLastError();
   }
+  if (G < 1 || G > kMaxG) return hipErrorInvalidValue;
   // one workgroup per CU, a multiple of the XCD count (the schedule assigns tiles per XCD)
   int64_t grid = (int64_t)num_cus;
   grid = (grid / kXcds) * kXcds;
@@ -709,7 +832,7 @@ hipError_t launch_gemm_fp8_silu_quantize(int32_t G, int64_t M, int64_t I, int64_
                                          const int32_t* offsets, const int32_t* valid, uint8_t* q, float* s,
                                          int num_cus, hipStream_t st) {
   if (M == 0 || I == 0) return hipSuccess;
-  if (I % 128 != 0 || K % BK != 0 || K / BK > kMaxKb) return hipErrorInvalidValue;
+  if (I % 128 != 0 || K % BK != 0 || K / BK > kMaxKb || G < 1 || G > kMaxG) return hipErrorInvalidValue;
   int64_t grid = (int64_t)num_cus;
   grid = (grid / kXcds) * kXcds;
   if (grid < kXcds * kSM) grid = kXcds * kSM;

@@ -199,14 +199,14 @@ fgg_status fgg_moe_permute_quantize(const int32_t* topk_ids, int64_t T, int32_t 
  *   their MFMA work is skipped in 64-row units (their A rows may still be
  *   read).  aq = {E4M3,F32,1,128}: a [M][K], a_scales [K/128][M];
  *   bq = {E4M3,F32,128,128}: b [G][N][K], b_scales [G][N/128][K/128].
- * FGG_LAYOUT_MASKED (decode): A is [G][M][K] (M = rows per group, <= 16);
+ * FGG_LAYOUT_MASKED (decode, K >= 128): A is [G][M][K] (M = rows per group, <= 16);
  *   group g uses rows m < masked_m[g] (values clamped to [0, M]); other rows
  *   are neither read nor written.  aq = {E4M3,F32,1,128}: a_scales
  *   [G][K/128][M].  bq = {E2M1X2,E8M0,1,32}: b [G][N][K/2],
  *   b_scales [G][N][K/32] uint8 (the E8M0 scale multiplies each 32-element
  *   block inside the MFMA); or bq = {E4M3,F32,128,128} as above.
  *   D is [G][M][ldd].
- * d: bf16, row stride ldd >= N.  N % 128 == 0, K % 128 == 0, 1 <= G <= 1024;
+ * d: bf16, row stride ldd >= N.  N % 128 == 0, K % 128 == 0 (K == 0 gives zeros), 1 <= G <= 1024;
  * the contiguous layout supports K <= 16384.
  * Device-side values of offsets / masked_m are trusted within these rules.
  */
@@ -258,7 +258,7 @@ fgg_status fgg_grouped_gemm_silu_quantize(int32_t G, int64_t M, int64_t I, int64
  *   The operands are dequantized on chip to fp16 (x·s rounded once) and
  *   contracted with fp16 MFMA in fp32; the rank-32 intermediate
  *   x_bf16 · l_down is accumulated in fp32 (bf16 MFMA) and rounded to bf16.
- *   Requires M % 128 == 0, K % 128 == 0, N % 128 == 0, rank in {0, 32}.
+ *   Requires M % 128 == 0, K % 128 == 0, K >= 128, N % 128 == 0, rank in {0, 32}.
  *   With a low-rank branch, workspace must hold fgg_scaled_gemm_workspace()
  *   bytes (the [M][32] intermediate and a [32][K] transposed copy of l_down).
  */

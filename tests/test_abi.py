@@ -101,6 +101,10 @@ def test_gemm_and_permute_reject_bad_arguments_on_host():
     epi = fgg.Epilogue(4096, 4096, 4096, 16, None)
     W = _q(fgg.Q_E2M1_1x16)
     assert lib.fgg_scaled_gemm(256, 128, 256, g, g, W, g, g, W, ctypes.byref(epi), g, 128, g, 1 << 20, None) == 2
+    # masked layout with K == 0 is not supported
+    assert lib.fgg_grouped_gemm_scaled(1, 2, 16, 128, 0, g, g, A, g, g, B4, None, g, g, 128, None) == 2
+    # W4A4 with K == 0 is not supported
+    assert lib.fgg_scaled_gemm(256, 128, 0, g, g, W, g, g, W, None, g, 128, None, 0, None) == 2
     # permute: bad k / E, missing workspace
     assert lib.fgg_moe_permute(g, 10, 0, 4, 128, None, None, 0, g, g, g, g, None, None, 100, g, 1 << 20, None) == 1
     assert lib.fgg_moe_permute(g, 10, 2, 2000, 128, None, None, 0, g, g, g, g, None, None, 100, g, 1 << 20, None) == 1

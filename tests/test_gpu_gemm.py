@@ -150,6 +150,29 @@ def test_grouped_contiguous_valid_counts(counts, masked, N, K):
     assert np.all(np.isnan(y[rest]))
 
 
+def test_k_zero_gives_zeros():
+    """K == 0: empty sums, so every computed output is +0 (and the SiLU requant of a
+    zero row is codes 0 with scale 1); nothing is fetched."""
+    G, N, M = 2, 256, 300
+    offsets = np.array([0, 128, 256], np.int32)
+    a = torch.zeros((M, 0), dtype=torch.uint8, device="cuda")
+    sa = torch.zeros((0, M), dtype=torch.float32, device="cuda")
+    b = torch.zeros((G, N, 0), dtype=torch.uint8, device="cuda")
+    sb = torch.zeros((G, N // 128, 0), dtype=torch.float32, device="cuda")
+    d = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device="cuda")
+    fgg.grouped_gemm_scaled(a, sa, b, sb, offsets=cuda(offsets), out=d)
+    y = to_np(d)
+    assert np.all(y[:256] == 0) and not np.any(np.signbit(y[:256])) and np.all(np.isnan(y[256:]))
+    yd = to_np(fgg.scaled_gemm(a, sa, b[0], sb[0]))
+    assert yd.shape == (M, N) and np.all(yd == 0)
+    q = torch.full((M, N // 2), 0xAB, dtype=torch.uint8, device="cuda")
+    s = torch.full((N // 256, M), -3.0, dtype=torch.float32, device="cuda")
+    fgg.grouped_gemm_silu_quantize(a, sa, b, sb, cuda(offsets), out=q, scales=s)
+    q, s = to_np(q), to_np(s)
+    assert np.all(q[:256] == 0) and np.all(s[:, :256] == 1.0)
+    assert np.all(q[256:] == 0xAB) and np.all(s[:, 256:] == -3.0)
+
+
 @pytest.mark.parametrize("M,N,K", [(500, 256, 1024), (128, 128, 128), (1, 128, 256)])
 def test_dense_small_and_one_group_identity(M, N, K):
     g = synth.rng(M + N + K)
