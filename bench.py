@@ -168,14 +168,18 @@ def bench_decode(fgg, synth, torch, iters=50, copies=3):
         for e in range(G):
             w = synth.normal_cuda(41_000 + 100 * c + e, (N, K), 0.02)
             fgg.quantize_blockwise(w, fgg.Q_E2M1_E8M0_1x32, out=bq[e], scales=be[e])
-        bqs.append(bq)
-        bes.append(be)
+        # offline: the weights in the tiled (MFMA operand order) layout the decode kernel streams
+        bt, st = fgg.pack_fp4_weights(bq, be)
+        del bq, be
+        bqs.append(bt)
+        bes.append(st)
     d = torch.empty((G, M, N), dtype=torch.bfloat16, device="cuda")
     ms = time_calls(lambda i: fgg.grouped_gemm_scaled(aq, sa, bqs[i % copies], bes[i % copies], masked_m=mm,
-                                                      b_qdesc=fgg.Q_E2M1_E8M0_1x32, out=d), iters, 5)
+                                                      b_qdesc=fgg.Q_E2M1_E8M0_1x32_TILED, out=d, n=N), iters, 5)
     wbytes = G * N * (K // 2) + G * N * (K // 32)
     gbs = wbytes / (ms * 1e-3) / 1e9
-    return dict(workload="moe_decode G=32 M=1..16 (U) N=4096 K=7168 E2M1+E8M0/32 weights, e4m3 1x128 acts",
+    return dict(workload="moe_decode G=32 M=1..16 (U) N=4096 K=7168 E2M1+E8M0/32 weights (tiled layout), "
+                         "e4m3 1x128 acts",
                 us_per_call=round(ms * 1e3, 2), weight_bytes=wbytes, value=round(gbs, 1), unit="GB/s",
                 pct_hbm_peak=round(100 * gbs / PEAK_HBM_GBS, 1))
 

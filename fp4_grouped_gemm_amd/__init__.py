@@ -14,16 +14,16 @@ import torch
 
 __all__ = [
     "FggError", "load_library", "library_path",
-    "Q_E4M3_1x128", "Q_E4M3_128x128", "Q_E2M1_1x16", "Q_E2M1_E8M0_1x32",
+    "Q_E4M3_1x128", "Q_E4M3_128x128", "Q_E2M1_1x16", "Q_E2M1_E8M0_1x32", "Q_E2M1_E8M0_1x32_TILED",
     "quantize_blockwise", "moe_permute", "moe_permute_outputs", "moe_permute_workspace_bytes",
-    "grouped_gemm_scaled",
+    "grouped_gemm_scaled", "grouped_gemm_silu_quantize", "pack_fp4_weights",
     "scaled_gemm", "moe_combine", "set_num_cus",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libfgg.so")
 
-FGG_F32, FGG_BF16, FGG_E4M3, FGG_E2M1X2, FGG_E8M0 = 0, 1, 2, 3, 4
+FGG_F32, FGG_BF16, FGG_E4M3, FGG_E2M1X2, FGG_E8M0, FGG_E2M1X2_TILED = 0, 1, 2, 3, 4, 5
 FGG_ACT_NONE, FGG_ACT_SILU_MUL = 0, 1
 FGG_LAYOUT_CONTIGUOUS, FGG_LAYOUT_MASKED = 0, 1
 _STATUS = {0: "FGG_OK", 1: "FGG_ERR_INVALID_VALUE", 2: "FGG_ERR_UNSUPPORTED", 3: "FGG_ERR_HIP"}
@@ -51,6 +51,7 @@ Q_E4M3_1x128 = (FGG_E4M3, FGG_F32, 1, 128)
 Q_E4M3_128x128 = (FGG_E4M3, FGG_F32, 128, 128)
 Q_E2M1_1x16 = (FGG_E2M1X2, FGG_F32, 1, 16)
 Q_E2M1_E8M0_1x32 = (FGG_E2M1X2, FGG_E8M0, 1, 32)
+Q_E2M1_E8M0_1x32_TILED = (FGG_E2M1X2_TILED, FGG_E8M0, 1, 32)   # masked-GEMM weights from pack_fp4_weights
 
 _lib = None
 
@@ -81,6 +82,8 @@ def load_library():
         "fgg_scaled_gemm_workspace": ([I64, I64, I64, QDesc, QDesc, ctypes.POINTER(Epilogue), ctypes.POINTER(SZ)], I32),
         "fgg_scaled_gemm": ([I64, I64, I64, P, P, QDesc, P, P, QDesc, ctypes.POINTER(Epilogue), P, I64, P, SZ, P], I32),
         "fgg_moe_combine": ([P, I64, P, P, I64, I32, I64, P, I64, P], I32),
+        "fgg_pack_fp4_weights_bytes": ([I32, I64, I64, ctypes.POINTER(SZ), ctypes.POINTER(SZ)], I32),
+        "fgg_pack_fp4_weights": ([P, P, I32, I64, I64, P, P, P], I32),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -228,15 +231,17 @@ def moe_permute(topk_ids: torch.Tensor, num_experts: int, align: int = 128, xq=N
 # --------------------------------------------------------------------- GEMMs
 
 def grouped_gemm_scaled(a, a_scales, b, b_scales, offsets=None, masked_m=None,
-                        b_qdesc=Q_E4M3_128x128, out=None):
+                        b_qdesc=Q_E4M3_128x128, out=None, n=None):
     """Contiguous layout when ``offsets`` is given (a [M, K], a_scales [K/128, M],
     b [G, N, K], b_scales [G, N/128, K/128]); masked layout when ``masked_m``
     is given (a [G, M, K], a_scales [G, K/128, M], b [G, N, K/2] with E8M0
     scales [G, N, K/32] for Q_E2M1_E8M0_1x32, or e4m3 as above).  With
     ``offsets``, an optional ``masked_m`` gives each group's real row count
     (the permute's counts): the padding rows past it are not written.
+    With Q_E2M1_E8M0_1x32_TILED (weights from pack_fp4_weights) ``n`` gives N.
     Returns bf16 [M, N] or [G, M, N]."""
-    G, N = b.shape[0], b.shape[1]
+    G = b.shape[0]
+    N = int(n) if n is not None else b.shape[1]
     dev = a.device
     if offsets is not None:
         M, K = a.shape
@@ -278,6 +283,29 @@ def grouped_gemm_silu_quantize(a, a_scales, b, b_scales, offsets, counts=None, o
         _ptr(offsets), _ptr(counts), _ptr(out), _ptr(scales), _stream(dev))
     _check("fgg_grouped_gemm_silu_quantize", st)
     return out, scales
+
+
+def pack_fp4_weights(b, b_scales, out=None, scales_out=None):
+    """Re-lay out FP4 expert weights for the masked GEMM (fgg_pack_fp4_weights):
+    b [G, N, K/2] uint8 E2M1 pairs and b_scales [G, N, K/32] uint8 E8M0 ->
+    (b_tiled uint8 [G, N*K/2], s_tiled uint8 [G, (N/16)*ceil(K/512)*256]), used with
+    b_qdesc=Q_E2M1_E8M0_1x32_TILED."""
+    G, N, Kh = b.shape
+    K = 2 * Kh
+    for t in (b, b_scales):
+        assert t.is_contiguous()
+    lib = load_library()
+    nb, ns = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    _check("fgg_pack_fp4_weights_bytes", lib.fgg_pack_fp4_weights_bytes(G, N, K, ctypes.byref(nb), ctypes.byref(ns)))
+    dev = b.device
+    if out is None:
+        out = torch.empty((G, nb.value // max(G, 1)), dtype=torch.uint8, device=dev)
+    if scales_out is None:
+        scales_out = torch.empty((G, ns.value // max(G, 1)), dtype=torch.uint8, device=dev)
+    assert out.numel() >= nb.value and scales_out.numel() >= ns.value
+    st = lib.fgg_pack_fp4_weights(_ptr(b), _ptr(b_scales), G, N, K, _ptr(out), _ptr(scales_out), _stream(dev))
+    _check("fgg_pack_fp4_weights", st)
+    return out, scales_out
 
 
 def scaled_gemm_workspace_bytes(M: int, N: int, K: int, qdesc: str = "fp8", rank: int = 0) -> int:

@@ -200,14 +200,16 @@ fgg_status fgg_grouped_gemm_scaled(fgg_layout layout, int32_t G, int64_t M, int6
                                               (uint16_t*)d, ldd, num_cus, (hipStream_t)stream));
   }
   if (layout == FGG_LAYOUT_MASKED) {
-    const bool fp4 = same_q(bq, FGG_E2M1X2, FGG_E8M0, 1, 32);
+    const bool tiled = same_q(bq, FGG_E2M1X2_TILED, FGG_E8M0, 1, 32);
+    const bool fp4 = tiled || same_q(bq, FGG_E2M1X2, FGG_E8M0, 1, 32);
     if (!fp4 && !same_q(bq, FGG_E4M3, FGG_F32, 128, 128)) return FGG_ERR_UNSUPPORTED;
     if (M > 16 || K == 0) return FGG_ERR_UNSUPPORTED;
     if (!masked_m) return FGG_ERR_INVALID_VALUE;
+    if (tiled && !aligned(b_scales, 16)) return FGG_ERR_INVALID_VALUE;
     fgg_status st = device_check(&num_cus);
     if (st != FGG_OK) return st;
     if (M == 0 || N == 0) return FGG_OK;
-    return finish(fgg::launch_gemm_masked(fp4, G, M, N, K, (const uint8_t*)a, (const float*)a_scales,
+    return finish(fgg::launch_gemm_masked(fp4, tiled, G, M, N, K, (const uint8_t*)a, (const float*)a_scales,
                                           (const uint8_t*)b, b_scales, masked_m, (uint16_t*)d, ldd,
                                           (hipStream_t)stream));
   }
@@ -290,6 +292,28 @@ fgg_status fgg_scaled_gemm(int64_t M, int64_t N, int64_t K, const void* a, const
                                    (uint16_t*)d, ldd, workspace, (hipStream_t)stream));
   }
   return FGG_ERR_UNSUPPORTED;
+}
+
+fgg_status fgg_pack_fp4_weights_bytes(int32_t G, int64_t N, int64_t K, size_t* b_bytes, size_t* s_bytes) {
+  if (G < 0 || N < 0 || K < 0 || !b_bytes || !s_bytes) return FGG_ERR_INVALID_VALUE;
+  if (N % 16 != 0 || K % 128 != 0) return FGG_ERR_UNSUPPORTED;
+  fgg::fp4_tiled_bytes(G, N, K, b_bytes, s_bytes);
+  return FGG_OK;
+}
+
+fgg_status fgg_pack_fp4_weights(const void* b, const void* b_scales, int32_t G, int64_t N, int64_t K,
+                                void* b_tiled, void* s_tiled, void* stream) {
+  if (G < 0 || N < 0 || K < 0) return FGG_ERR_INVALID_VALUE;
+  if (N % 16 != 0 || K % 128 != 0) return FGG_ERR_UNSUPPORTED;
+  const bool empty = G == 0 || N == 0 || K == 0;
+  if (!empty && (!b || !b_scales || !b_tiled || !s_tiled)) return FGG_ERR_INVALID_VALUE;
+  if (!aligned(b, 16) || !aligned(b_tiled, 16) || !aligned(s_tiled, 16)) return FGG_ERR_INVALID_VALUE;
+  int num_cus = 0;
+  fgg_status st = device_check(&num_cus);
+  if (st != FGG_OK) return st;
+  if (empty) return FGG_OK;
+  return finish(fgg::launch_pack_fp4(G, N, K, (const uint8_t*)b, (const uint8_t*)b_scales, (uint8_t*)b_tiled,
+                                     (uint8_t*)s_tiled, num_cus, (hipStream_t)stream));
 }
 
 fgg_status fgg_moe_combine(const void* y, int64_t ldy, const int32_t* src_to_row, const float* topk_w, int64_t T,

@@ -44,9 +44,15 @@ hipError_t launch_gemm_fp8_silu_quantize(int32_t G, int64_t M, int64_t I, int64_
                                          int num_cus, hipStream_t st);
 
 // Masked (decode) layout, A e4m3 1x128; B either E2M1x2 + E8M0/32 or e4m3 128x128.
-hipError_t launch_gemm_masked(bool b_fp4, int32_t G, int64_t M, int64_t N, int64_t K,
+hipError_t launch_gemm_masked(bool b_fp4, bool tiled, int32_t G, int64_t M, int64_t N, int64_t K,
                               const uint8_t* a, const float* sa, const uint8_t* b, const void* sb,
                               const int32_t* masked_m, uint16_t* d, int64_t ldd, hipStream_t st);
+
+// FP4 weight tiling for the decode kernel: codes [G][N][K/2] and E8M0 scales [G][N][K/32]
+// to FGG_E2M1X2_TILED codes and their scale spans (sizes from fp4_tiled_bytes).
+void fp4_tiled_bytes(int32_t G, int64_t N, int64_t K, size_t* b_bytes, size_t* s_bytes);
+hipError_t launch_pack_fp4(int32_t G, int64_t N, int64_t K, const uint8_t* b, const uint8_t* s, uint8_t* bt,
+                           uint8_t* st, int num_cus, hipStream_t stream);
 
 // W4A4: E2M1 x E2M1 with fp32 per-16 scales, optional rank-r low-rank branch and bias.
 size_t w4a4_workspace_bytes(int64_t M, int64_t K, int32_t rank);

@@ -54,7 +54,10 @@ typedef enum {
   FGG_BF16 = 1,
   FGG_E4M3 = 2,
   FGG_E2M1X2 = 3,
-  FGG_E8M0 = 4
+  FGG_E8M0 = 4,
+  /* E2M1 codes packed as FGG_E2M1X2, stored in 16-row x 128-K tiles in MFMA operand
+   * order (weights of the masked FP4 GEMM only; see fgg_pack_fp4_weights) */
+  FGG_E2M1X2_TILED = 5
 } fgg_dtype;
 
 /* Quantization descriptor: code type, scale type and the block one scale covers. */
@@ -204,7 +207,10 @@ fgg_status fgg_moe_permute_quantize(const int32_t* topk_ids, int64_t T, int32_t 
  *   are neither read nor written.  aq = {E4M3,F32,1,128}: a_scales
  *   [G][K/128][M].  bq = {E2M1X2,E8M0,1,32}: b [G][N][K/2],
  *   b_scales [G][N][K/32] uint8 (the E8M0 scale multiplies each 32-element
- *   block inside the MFMA); or bq = {E4M3,F32,128,128} as above.
+ *   block inside the MFMA); or bq = {E2M1X2_TILED,E8M0,1,32}: the same weights
+ *   re-laid out by fgg_pack_fp4_weights (b_scales 16-byte aligned), the same
+ *   results bit for bit and a contiguous 1 KB per weight load; or
+ *   bq = {E4M3,F32,128,128} as above.
  *   D is [G][M][ldd].
  * d: bf16, row stride ldd >= N.  N % 128 == 0, K % 128 == 0 (K == 0 gives zeros), 1 <= G <= 1024;
  * the contiguous layout supports K <= 16384.
@@ -243,6 +249,31 @@ fgg_status fgg_grouped_gemm_silu_quantize(int32_t G, int64_t M, int64_t I, int64
                                           const void* a_scales, fgg_qdesc aq, const void* b, const void* b_scales,
                                           fgg_qdesc bq, const int32_t* offsets, const int32_t* counts,
                                           void* q_out, float* s_out, void* stream);
+
+/*
+ * fgg_pack_fp4_weights — offline re-layout of FP4 expert weights for the masked
+ * (decode) GEMM.
+ *
+ * [FP4MoE] "Blackwell架构下FP4 MoE模型的TFLOPS性能优化" §2.1: FP4 data should be
+ * aligned to 128-bit boundaries and stored interleaved for the tensor-core path;
+ * §3.1: a dedicated packed weight format.  The interleave chosen here is the
+ * gfx950 MFMA operand order, so that one wave's load of one K block of 16 weight
+ * rows is a contiguous 1 KB.  A pure byte permutation of
+ *   b [G][N][K/2] (FGG_E2M1X2 codes) and b_scales [G][N][K/32] (E8M0):
+ *   b_tiled: for g, nb = n / 16, kb = K block (128 elements, 64 bytes of a row),
+ *     tile (g, nb, kb) is 1024 bytes at ((g·N/16 + nb)·(K/128) + kb)·1024; its
+ *     16-byte piece 16c + r (c = 0..3, r = 0..15) holds row 16·nb + r, bytes
+ *     [64·kb + 16·c, +16) of that row (K elements [128·kb + 32·c, +32)).
+ *   s_tiled: for span j = 16 scale bytes of a row (4 K blocks), span (g, nb, j) is
+ *     256 bytes at ((g·N/16 + nb)·ceil(K/512) + j)·256; bytes [16·r, 16·r + 16) hold
+ *     row 16·nb + r's scale bytes [16·j, 16·j + 16), and 127 (2^0) past K/32.
+ * Sizes from fgg_pack_fp4_weights_bytes: G·N·K/2 and G·(N/16)·ceil(K/512)·256 bytes.
+ * Requires N % 16 == 0, K % 128 == 0 (else FGG_ERR_UNSUPPORTED); b, b_tiled and
+ * s_tiled 16-byte aligned.  b_tiled / s_tiled must not overlap the inputs.
+ */
+fgg_status fgg_pack_fp4_weights_bytes(int32_t G, int64_t N, int64_t K, size_t* b_bytes, size_t* s_bytes);
+fgg_status fgg_pack_fp4_weights(const void* b, const void* b_scales, int32_t G, int64_t N, int64_t K,
+                                void* b_tiled, void* s_tiled, void* stream);
 
 /*
  * fgg_scaled_gemm — the dense one-group case ([MegaMoE] §2.1 fp8_gemm with

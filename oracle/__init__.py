@@ -59,6 +59,8 @@ from .formats import (  # noqa: F401
     bf16_bits,
     pack_e2m1x2,
     unpack_e2m1x2,
+    tile_fp4_weights,
+    untile_fp4_weights,
 )
 from .quantize import (  # noqa: F401
     quantize_e4m3_blocks,

@@ -141,3 +141,67 @@ def bf16_bits(x) -> np.ndarray:
     bits = f.view(np.uint32)
     assert np.all((bits & 0xFFFF) == 0) or np.any(np.isnan(v)), "not a bf16 value"
     return (bits >> 16).astype(np.uint16)
+
+
+# --------------------------------------------------------------- tiled FP4 layout
+# [FP4MoE] §2.1 asks for FP4 data aligned to 128-bit boundaries in an interleaved
+# storage format, §3.1 for a dedicated packed weight format.  The library's
+# interleave (its header's FGG_E2M1X2_TILED) is stated per 16-row group `nb` of
+# an expert `g` and per 128-element K block `kb` (64 bytes of a packed row):
+#   a 1024-byte tile, whose 16-byte piece number 16·c + r (c = 0..3, r = 0..15) is
+#   row 16·nb + r's packed bytes [64·kb + 16·c, 64·kb + 16·c + 16);
+# and for the E8M0 scales per span j of 16 scale bytes (4 K blocks):
+#   a 256-byte span, whose bytes [16·r, 16·r + 16) are row 16·nb + r's scale
+#   bytes [16·j, 16·j + 16), the positions past the row's K/32 bytes holding 127.
+# Tiles and spans follow each other in (g, nb, kb) and (g, nb, j) order.
+
+def tile_fp4_weights(b, b_scales):
+    """b uint8 [G, N, K/2], b_scales uint8 [G, N, K/32] ->
+    (codes uint8 [G·N·K/2], scales uint8 [G·(N/16)·ceil(K/512)·256]), piece by
+    piece as stated above."""
+    b = np.asarray(b, dtype=np.uint8)
+    s = np.asarray(b_scales, dtype=np.uint8)
+    G, N, Kh = b.shape
+    nkb, nsc = Kh // 64, s.shape[2]
+    nspan = -(-nsc // 16)
+    assert N % 16 == 0 and Kh % 64 == 0 and s.shape[:2] == (G, N)
+    codes = np.empty(G * N * Kh, dtype=np.uint8)
+    scales = np.full(G * (N // 16) * nspan * 256, 127, dtype=np.uint8)
+    for g in range(G):
+        for nb in range(N // 16):
+            for kb in range(nkb):
+                tile = ((g * (N // 16) + nb) * nkb + kb) * 1024
+                for c in range(4):
+                    for r in range(16):
+                        piece = tile + (16 * c + r) * 16
+                        codes[piece:piece + 16] = b[g, 16 * nb + r, 64 * kb + 16 * c:64 * kb + 16 * c + 16]
+            for j in range(nspan):
+                span = ((g * (N // 16) + nb) * nspan + j) * 256
+                for r in range(16):
+                    row = s[g, 16 * nb + r, 16 * j:16 * j + 16]
+                    scales[span + 16 * r:span + 16 * r + len(row)] = row
+    return codes, scales
+
+
+def untile_fp4_weights(codes, scales, G, N, K):
+    """Inverse of tile_fp4_weights: -> (b [G, N, K/2], b_scales [G, N, K/32])."""
+    codes = np.asarray(codes, dtype=np.uint8).reshape(-1)
+    scales = np.asarray(scales, dtype=np.uint8).reshape(-1)
+    Kh, nsc = K // 2, K // 32
+    nkb, nspan = K // 128, -(-nsc // 16)
+    b = np.empty((G, N, Kh), dtype=np.uint8)
+    s = np.empty((G, N, nsc), dtype=np.uint8)
+    for g in range(G):
+        for nb in range(N // 16):
+            for kb in range(nkb):
+                tile = ((g * (N // 16) + nb) * nkb + kb) * 1024
+                for c in range(4):
+                    for r in range(16):
+                        piece = tile + (16 * c + r) * 16
+                        b[g, 16 * nb + r, 64 * kb + 16 * c:64 * kb + 16 * c + 16] = codes[piece:piece + 16]
+            for j in range(nspan):
+                span = ((g * (N // 16) + nb) * nspan + j) * 256
+                for r in range(16):
+                    n_here = min(16, nsc - 16 * j)
+                    s[g, 16 * nb + r, 16 * j:16 * j + n_here] = scales[span + 16 * r:span + 16 * r + n_here]
+    return b, s

@@ -27,6 +27,7 @@ def test_header_declares_the_boundary():
     names = _declared()
     for n in ["fgg_quantize_blockwise", "fgg_moe_permute", "fgg_moe_permute_workspace", "fgg_moe_permute_quantize",
               "fgg_grouped_gemm_scaled", "fgg_grouped_gemm_silu_quantize",
+              "fgg_pack_fp4_weights_bytes", "fgg_pack_fp4_weights",
               "fgg_scaled_gemm", "fgg_scaled_gemm_workspace", "fgg_moe_combine", "fgg_status_string",
               "fgg_last_hip_error", "fgg_set_num_cus"]:
         assert n in names
@@ -103,6 +104,15 @@ def test_gemm_and_permute_reject_bad_arguments_on_host():
     assert lib.fgg_scaled_gemm(256, 128, 256, g, g, W, g, g, W, ctypes.byref(epi), g, 128, g, 1 << 20, None) == 2
     # masked layout with K == 0 is not supported
     assert lib.fgg_grouped_gemm_scaled(1, 2, 16, 128, 0, g, g, A, g, g, B4, None, g, g, 128, None) == 2
+    # FP4 weight tiling: sizes, N not a multiple of 16, K not a multiple of 128, misaligned output
+    nb, ns = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    assert lib.fgg_pack_fp4_weights_bytes(2, 4096, 7168, ctypes.byref(nb), ctypes.byref(ns)) == 0
+    assert nb.value == 2 * 4096 * 3584 and ns.value == 2 * 256 * 14 * 256
+    assert lib.fgg_pack_fp4_weights_bytes(1, 32, 384, ctypes.byref(nb), ctypes.byref(ns)) == 0
+    assert nb.value == 32 * 192 and ns.value == 2 * 1 * 256
+    assert lib.fgg_pack_fp4_weights_bytes(1, 40, 384, ctypes.byref(nb), ctypes.byref(ns)) == 2
+    assert lib.fgg_pack_fp4_weights(g, g, 1, 32, 200, g, g, None) == 2
+    assert lib.fgg_pack_fp4_weights(g, g, 1, 32, 256, ctypes.c_void_p(g.value + 8), g, None) == 1
     # W4A4 with K == 0 is not supported
     assert lib.fgg_scaled_gemm(256, 128, 0, g, g, W, g, g, W, None, g, 128, None, 0, None) == 2
     # permute: bad k / E, missing workspace

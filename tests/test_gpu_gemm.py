@@ -381,6 +381,58 @@ def test_masked_fp4_full_size_sampled():
         tol_check(y[e, :m], ref[0, :m], what=f"decode expert {e}")
 
 
+@pytest.mark.parametrize("G,M,N,K,masked", [(3, 16, 256, 1024, [16, 0, 9]), (2, 7, 128, 384, [7, 3]),
+                                            (1, 16, 128, 640, [1])])
+def test_masked_fp4_tiled_equals_plain(G, M, N, K, masked):
+    """Weights re-laid out by pack_fp4_weights: the packer matches the oracle's
+    statement of the layout byte for byte (including the 127 padding of partial
+    scale spans), and the masked GEMM on the tiled weights equals the one on the
+    plain weights bit for bit (the same operands reach the same MFMAs)."""
+    x, w, _ = _masked_case(G, M, N, K, G * 77 + N + K)
+    mm = np.array(masked, np.int32)
+    aq, sa = _quant_masked_a_gpu(x)
+    bq, be = _quant_weights_gpu(w, fgg.Q_E2M1_E8M0_1x32)
+    bt, st = fgg.pack_fp4_weights(bq, be)
+    codes_r, scales_r = oracle.tile_fp4_weights(to_np(bq), to_np(be))
+    assert np.array_equal(to_np(bt).reshape(-1), codes_r) and np.array_equal(to_np(st).reshape(-1), scales_r)
+    d1 = torch.full((G, M, N), float("nan"), dtype=torch.bfloat16, device="cuda")
+    d2 = torch.full((G, M, N), float("nan"), dtype=torch.bfloat16, device="cuda")
+    fgg.grouped_gemm_scaled(aq, sa, bq, be, masked_m=cuda(mm), b_qdesc=fgg.Q_E2M1_E8M0_1x32, out=d1)
+    fgg.grouped_gemm_scaled(aq, sa, bt, st, masked_m=cuda(mm), b_qdesc=fgg.Q_E2M1_E8M0_1x32_TILED, out=d2, n=N)
+    y1, y2 = to_np(d1), to_np(d2)
+    for e in range(G):
+        m = int(mm[e])
+        assert np.array_equal(y2[e, :m], y1[e, :m])
+        assert np.all(np.isnan(y2[e, m:]))
+
+
+def test_masked_fp4_tiled_full_size():
+    """Decode shape (32 experts, N 4096, K 7168): tiled and plain layouts give the
+    same outputs bit for bit; sampled tiles of the packed weights match the oracle."""
+    wl = synth.moe_decode(with_weights=False)
+    G, M, N, K = wl["G"], wl["M_max"], wl["N"], wl["K"]
+    mm = wl["masked_m"]
+    aq, sa = _quant_masked_a_gpu(wl["x"])
+    bq = torch.empty((G, N, K // 2), dtype=torch.uint8, device="cuda")
+    be = torch.empty((G, N, K // 32), dtype=torch.uint8, device="cuda")
+    for e in range(G):
+        we = synth.moe_decode_expert_weight(1004, e, N, K)
+        fgg.quantize_blockwise(cuda(we), fgg.Q_E2M1_E8M0_1x32, out=bq[e], scales=be[e])
+    bt, st = fgg.pack_fp4_weights(bq, be)
+    y1 = fgg.grouped_gemm_scaled(aq, sa, bq, be, masked_m=cuda(mm), b_qdesc=fgg.Q_E2M1_E8M0_1x32)
+    y2 = fgg.grouped_gemm_scaled(aq, sa, bt, st, masked_m=cuda(mm), b_qdesc=fgg.Q_E2M1_E8M0_1x32_TILED, n=N)
+    for e in range(G):
+        assert torch.equal(y2[e, :int(mm[e])], y1[e, :int(mm[e])])
+    # experts 5 and 30, rows 1024..1055 (two 16-row groups), all K, against the oracle's layout
+    for e in (5, 30):
+        cr, sr = oracle.tile_fp4_weights(to_np(bq[e:e + 1, 1024:1056]), to_np(be[e:e + 1, 1024:1056]))
+        tile_bytes, span_bytes = (K // 128) * 1024, ((K // 32 + 15) // 16) * 256
+        g0 = e * (N // 16) + 1024 // 16                      # first 16-row group of the sample
+        got_c = to_np(bt).reshape(-1)[g0 * tile_bytes:(g0 + 2) * tile_bytes]
+        got_s = to_np(st).reshape(-1)[g0 * span_bytes:(g0 + 2) * span_bytes]
+        assert np.array_equal(got_c, cr) and np.array_equal(got_s, sr)
+
+
 def test_masked_fp8_equals_contiguous():
     G, M, N, K = 3, 16, 256, 512
     x, w, mm = _masked_case(G, M, N, K, 4242, np.array([16, 3, 11], np.int32))

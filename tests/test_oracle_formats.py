@@ -137,3 +137,43 @@ def test_round_bf16_single_rounding_from_float64():
     v = np.array([1 + 2.0 ** -8, 1 + 2.0 ** -8 + 2.0 ** -40, -(1 + 3 * 2.0 ** -8)])
     assert oracle.round_bf16(v).tolist() == [1.0, 1 + 2.0 ** -7, -(1 + 2 * 2.0 ** -7)]
     assert oracle.bf16_bits(np.array([1.0, -2.0])).tolist() == [0x3F80, 0xC000]
+
+
+# ------------------------------------------------------------- tiled FP4 weights
+
+@pytest.mark.parametrize("G,N,K", [(2, 32, 384), (1, 16, 1024), (3, 48, 640)])
+def test_tile_fp4_weights_is_a_permutation_with_padding(G, N, K):
+    """The tiled codes are a permutation of the packed codes, the tiled scales
+    hold every scale byte once plus 127-padding to whole 16-byte spans, and
+    untiling restores both arrays."""
+    rng = np.random.default_rng(G * 1000 + N + K)
+    b = rng.integers(0, 256, size=(G, N, K // 2), dtype=np.uint8)
+    s = rng.integers(100, 140, size=(G, N, K // 32), dtype=np.uint8)
+    codes, scales = oracle.tile_fp4_weights(b, s)
+    nspan = -(-(K // 32) // 16)
+    assert codes.size == b.size and scales.size == G * (N // 16) * nspan * 256
+    assert np.array_equal(np.sort(codes), np.sort(b.reshape(-1)))
+    pad = scales.size - s.size
+    assert np.count_nonzero(scales == 127) == np.count_nonzero(s == 127) + pad
+    assert np.array_equal(np.sort(scales[scales != 127]), np.sort(s[s != 127]))
+    b2, s2 = oracle.untile_fp4_weights(codes, scales, G, N, K)
+    assert np.array_equal(b2, b) and np.array_equal(s2, s)
+
+
+def test_tile_fp4_weights_worked_positions():
+    """Worked example of the stated layout: in a [1, 32, 256] weight (2 K blocks of
+    64 bytes per row, two 16-row groups), the byte of row 21 (group 1, r = 5) at
+    packed position 100 (K block 1, 16-byte chunk c = 2, byte 4) sits in tile
+    (nb 1, kb 1) = 3, piece 16·2 + 5 = 37: offset 3·1024 + 37·16 + 4 = 3668.  Its
+    scale byte 6 (of 8 per row: span 0) sits at span (nb 1, j 0) = 1, row 5, byte 6:
+    offset 256 + 5·16 + 6 = 342; bytes 8..15 of every row's span are padding (127)."""
+    b = np.zeros((1, 32, 128), np.uint8)
+    s = np.zeros((1, 32, 8), np.uint8)
+    b[0, 21, 100] = 0xA5
+    s[0, 21, 6] = 0x81
+    codes, scales = oracle.tile_fp4_weights(b, s)
+    assert np.flatnonzero(codes).tolist() == [3668] and codes[3668] == 0xA5
+    assert scales[342] == 0x81
+    assert np.count_nonzero(scales == 0x81) == 1
+    spans = scales.reshape(2, 16, 16)
+    assert np.all(spans[:, :, 8:] == 127) and np.count_nonzero(spans[:, :, :8]) == 1
