@@ -238,12 +238,10 @@ fgg_status fgg_grouped_gemm_silu_quantize(int32_t G, int64_t M, int64_t I, int64
 
 fgg_status fgg_scaled_gemm_workspace(int64_t M, int64_t N, int64_t K, fgg_qdesc aq, fgg_qdesc bq,
                                      const fgg_epilogue* epi, size_t* bytes) {
-  (void)N;
-  (void)K;
-  if (!bytes || M < 0) return FGG_ERR_INVALID_VALUE;
+  if (!bytes || M < 0 || N < 0 || K < 0) return FGG_ERR_INVALID_VALUE;
   *bytes = 0;
-  if (same_q(aq, FGG_E2M1X2, FGG_F32, 1, 16) && same_q(bq, FGG_E2M1X2, FGG_F32, 1, 16) && epi && epi->rank > 0)
-    *bytes = fgg::w4a4_workspace_bytes(M, K, epi->rank);
+  if (same_q(aq, FGG_E2M1X2, FGG_F32, 1, 16) && same_q(bq, FGG_E2M1X2, FGG_F32, 1, 16))
+    *bytes = fgg::w4a4_workspace_bytes(M, N, K, epi ? epi->rank : 0);
   return FGG_OK;
 }
 
@@ -277,9 +275,10 @@ fgg_status fgg_scaled_gemm(int64_t M, int64_t N, int64_t K, const void* a, const
       if (!epi->x_bf16 || !epi->l_down || !epi->l_up) return FGG_ERR_INVALID_VALUE;
       if (!aligned(epi->x_bf16, 16) || !aligned(epi->l_down, 2) || !aligned(epi->l_up, 2))
         return FGG_ERR_INVALID_VALUE;
-      if (!workspace || ws_bytes < fgg::w4a4_workspace_bytes(M, K, rank) || !aligned(workspace, 16))
-        return FGG_ERR_INVALID_VALUE;
     }
+    if (M > 0 && N > 0 &&
+        (!workspace || ws_bytes < fgg::w4a4_workspace_bytes(M, N, K, rank) || !aligned(workspace, 256)))
+      return FGG_ERR_INVALID_VALUE;
     const void* bias = epi ? epi->bias : nullptr;
     if (bias && !aligned(bias, 2)) return FGG_ERR_INVALID_VALUE;
     fgg_status st = device_check(&num_cus);
@@ -289,7 +288,7 @@ fgg_status fgg_scaled_gemm(int64_t M, int64_t N, int64_t K, const void* a, const
                                    (const float*)b_scales, rank ? (const uint16_t*)epi->x_bf16 : nullptr,
                                    rank ? (const uint16_t*)epi->l_down : nullptr,
                                    rank ? (const uint16_t*)epi->l_up : nullptr, rank, (const uint16_t*)bias,
-                                   (uint16_t*)d, ldd, workspace, (hipStream_t)stream));
+                                   (uint16_t*)d, ldd, workspace, num_cus, (hipStream_t)stream));
   }
   return FGG_ERR_UNSUPPORTED;
 }

@@ -55,10 +55,10 @@ hipError_t launch_pack_fp4(int32_t G, int64_t N, int64_t K, const uint8_t* b, co
                            uint8_t* st, int num_cus, hipStream_t stream);
 
 // W4A4: E2M1 x E2M1 with fp32 per-16 scales, optional rank-r low-rank branch and bias.
-size_t w4a4_workspace_bytes(int64_t M, int64_t K, int32_t rank);
+size_t w4a4_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t rank);
 hipError_t launch_w4a4(int64_t M, int64_t N, int64_t K, const uint8_t* a, const float* sa,
                        const uint8_t* b, const float* sb, const uint16_t* x_bf16,
                        const uint16_t* l_down, const uint16_t* l_up, int32_t rank,
-                       const uint16_t* bias, uint16_t* d, int64_t ldd, void* ws, hipStream_t st);
+                       const uint16_t* bias, uint16_t* d, int64_t ldd, void* ws, int num_cus, hipStream_t st);
 
 }  // namespace fgg

@@ -6,16 +6,25 @@
 //
 // gfx950 has no matrix instruction that applies an arbitrary fp32 scale per 16
 // elements, and promoting 16-wide partial sums on the vector ALU would cost
-// M·N·K/16 FMAs (more than the matrix work).  So each operand tile is
-// dequantized once on its way into LDS, x·s rounded to fp16, and contracted
-// with v_mfma_f32_16x16x32_f16 in fp32.  The low-rank branch is a separate
-// small bf16-MFMA kernel for T = X·L_down (fp32 accumulate, stored bf16 in
-// the workspace, with L_down transposed there first) and one extra bf16 MFMA
-// step T·L_up per output tile, before the bias is added in the epilogue.
+// M·N·K/16 FMAs (more than the matrix work).  So each operand is dequantized
+// once, x·s rounded to fp16, into the workspace (w4a4_prep_kernel: every
+// element exactly once; dequantizing inside the GEMM made each workgroup redo
+// the tiles it shares with N/128 or M/128 others and left the kernel bound by
+// that vector-ALU work), and contracted with v_mfma_f32_16x16x32_f16 in fp32.
+// The low-rank branch is a separate small bf16-MFMA kernel for T = X·L_down
+// (fp32 accumulate, stored bf16 in the workspace, with L_down transposed there
+// first) and one extra bf16 MFMA step T·L_up per output tile, before the bias
+// is added in the epilogue.
 //
-// Tile: 128 x 128 per 256-thread workgroup (4 waves of 64 x 64); one 128-wide
-// K block per LDS stage (2 x 128 x 128 fp16 = 64 KB); 16-byte chunks of each
-// 256-byte LDS row are XOR-swizzled by the row index.
+// GEMM tile: 128 x 128 per 512-thread workgroup: 8 waves, each a 64 x 64 quadrant
+// and one of the two 32-wide halves of every K stage (two waves per SIMD; the two
+// halves' fp32 sums are added through LDS at the end); a 4-buffer LDS ring of
+// 64-wide K stages (A and B, 2 x 128 rows x 128 bytes of fp16 = 32 KB each)
+// filled by global_load_lds_dwordx4 with three stages in flight; each 128-byte
+// row's 16-byte chunks XOR-swizzled by the row index.
+#include <algorithm>
+#include <type_traits>
+
 #include "fgg_device.hpp"
 #include "fgg_internal.hpp"
 
@@ -24,8 +33,14 @@ namespace fgg {
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 
 namespace {
-constexpr int BM = 128, BN = 128, BK = 128;
-constexpr int kRowBytes = BK * 2;   // fp16 row in LDS
+constexpr int BM = 128, BN = 128;
+constexpr int BKH = 64;                       // K elements per LDS stage
+constexpr int kRowBytes = BKH * 2;            // one fp16 row of a stage: 128 bytes
+constexpr int kTileBytes = BM * kRowBytes;    // 16 KB (A or B)
+constexpr int kStageBytes = 2 * kTileBytes;   // A then B
+constexpr int kStages = 4;
+constexpr int kWaves = 8;                     // 2 x 2 output quadrants x 2 halves of each K stage
+constexpr int kDmaPerStage = kStageBytes / 1024 / kWaves;   // 1 KB DMA instructions per wave per stage
 
 __device__ inline float e2m1_f32(uint32_t nib, float s) {
   const uint32_t mag = nib & 7u;
@@ -56,17 +71,63 @@ __device__ inline void dequant32(uint4 packed, float s0, float s1, uint4* out4) 
   out4[3] = make_uint4(h[12], h[13], h[14], h[15]);
 }
 
-__device__ inline int swz16(int row) { return row & 15; }
+// 16-byte chunk swizzle of a 128-byte row (as in the FP8 GEMM): rows 16 apart share a
+// key; any 8 consecutive rows get 8 distinct keys
+__device__ inline int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+
+__device__ inline void dma16(const void* sbase, uint32_t voff, uint32_t lds) {
+  uint32_t save;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(save)
+      : "v"(voff), "s"(sbase), "s"(lds)
+      : "memory");
+}
+
+template <int N>
+__device__ inline void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
 }  // namespace
 
-// L_down [K][32] -> LdT [32][K] (bf16), so that both operands of T = X·L_down
-// are K-contiguous.
-__global__ void __launch_bounds__(256) w4a4_ld_transpose_kernel(const uint16_t* __restrict__ Ld, int64_t K,
-                                                                uint16_t* __restrict__ LdT) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;   // over K*32, rank fastest (coalesced reads)
-  if (i >= K * 32) return;
-  const int64_t k = i >> 5, r = i & 31;
-  LdT[r * K + k] = Ld[i];
+// The GEMM's operand preparation in one launch, by block ranges: packed E2M1 rows with
+// fp32 scales per 16 -> fp16 (x·s rounded once), for A ([M][K/2] -> [M][K]) and B,
+// one thread per 32 elements; then, with the low-rank branch, L_down [K][32] ->
+// LdT [32][K] (bf16), so that both operands of T = X·L_down are K-contiguous.
+__device__ inline void dequant_item(const uint8_t* __restrict__ q, const float* __restrict__ s, int64_t i,
+                                    uint16_t* __restrict__ out) {
+  const uint4 p = *reinterpret_cast<const uint4*>(q + i * 16);
+  const float2 sc = *reinterpret_cast<const float2*>(s + i * 2);
+  uint4 h[4];
+  dequant32(p, sc.x, sc.y, h);
+  uint4* o = reinterpret_cast<uint4*>(out + i * 32);
+  o[0] = h[0];
+  o[1] = h[1];
+  o[2] = h[2];
+  o[3] = h[3];
+}
+
+__global__ void __launch_bounds__(256) w4a4_prep_kernel(const uint8_t* __restrict__ qa, const float* __restrict__ sa,
+                                                        int64_t na, uint16_t* __restrict__ ah,
+                                                        const uint8_t* __restrict__ qb, const float* __restrict__ sb,
+                                                        int64_t nb, uint16_t* __restrict__ bh,
+                                                        const uint16_t* __restrict__ Ld, int64_t nld,
+                                                        uint16_t* __restrict__ LdT, int64_t K) {
+  const int64_t ba = (na + 255) / 256, bb = (nb + 255) / 256;
+  const int64_t blk = blockIdx.x;
+  if (blk < ba) {
+    const int64_t i = blk * 256 + threadIdx.x;
+    if (i < na) dequant_item(qa, sa, i, ah);
+  } else if (blk < ba + bb) {
+    const int64_t i = (blk - ba) * 256 + threadIdx.x;
+    if (i < nb) dequant_item(qb, sb, i, bh);
+  } else {
+    const int64_t i = (blk - ba - bb) * 256 + threadIdx.x;   // over K*32, rank fastest (coalesced reads)
+    if (i < nld) LdT[(i & 31) * K + (i >> 5)] = Ld[i];
+  }
 }
 
 // T[m][r] = Σ_k X[m][k] · L_down[k][r] (rank 32), fp32 accumulate, stored bf16.
@@ -127,25 +188,40 @@ __global__ void __launch_bounds__(256) w4a4_lowrank_down_kernel(const uint16_t* 
                                                  (uint32_t)bf16_bits_rne(s1[2]) | ((uint32_t)bf16_bits_rne(s1[3]) << 16));
 }
 
-__global__ void __launch_bounds__(256, 1)
-w4a4_gemm_kernel(int64_t M, int64_t N, int64_t K, const uint8_t* __restrict__ A, const float* __restrict__ SA,
-                 const uint8_t* __restrict__ B, const float* __restrict__ SB,
+__global__ void __launch_bounds__(512, 1)
+w4a4_gemm_kernel(int64_t M, int64_t N, int64_t K, const uint16_t* __restrict__ Ah, const uint16_t* __restrict__ Bh,
                  const uint16_t* __restrict__ T, const uint16_t* __restrict__ Lu, int rank,
                  const uint16_t* __restrict__ bias, uint16_t* __restrict__ D, int64_t ldd) {
-  __shared__ __align__(16) uint8_t smem[2 * BM * kRowBytes];   // A tile then B tile, fp16
-  uint8_t* at = smem;
-  uint8_t* bt = smem + BM * kRowBytes;
+  __shared__ __align__(16) uint8_t smem[kStages * kStageBytes];
+  const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int wm = wave & 1, wn = wave >> 1;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave & 1, wn = (wave >> 1) & 1, kw = wave >> 2;
   const int l16 = lane & 15, q = lane >> 4;
   const int64_t n_tiles = N / BN;
   const int64_t m0 = (blockIdx.x / n_tiles) * BM, n0 = (blockIdx.x % n_tiles) * BN;
-  const int64_t ng = K / 16;
-  const int nkb = (int)(K / BK);
+  const int nks = (int)(K / BKH);
 
-  // copy assignment: 128 rows x 4 chunks of 32 elements; thread t: chunk t%4, rows t/4 + 64i
-  const int cc = tid & 3, cr0 = tid >> 2;
+  // DMA roles: a stage is 32 segments of 1 KB (8 rows of 128 bytes): segments 0-15 the A
+  // rows, 16-31 the B rows; wave w issues segments 4w .. 4w+3.  Lane l fills chunk l % 8 of
+  // row l / 8 of its segment and reads source chunk (l % 8) ^ swz(row).
+  const int lrow = lane >> 3;
+  const uint8_t* Abase = reinterpret_cast<const uint8_t*>(Ah + m0 * K);
+  const uint8_t* Bbase = reinterpret_cast<const uint8_t*>(Bh + n0 * K);
+  uint32_t voff[kDmaPerStage];
+#pragma unroll
+  for (int i = 0; i < kDmaPerStage; ++i) {
+    const int seg = (wave * kDmaPerStage + i) & 15;
+    const int row = seg * 8 + lrow;
+    voff[i] = (uint32_t)row * (uint32_t)(K * 2) + (uint32_t)((((lane & 7) ^ swz(row))) * 16);
+  }
+  auto issue = [&](int ks, int stage) {
+    const uint8_t* src = (wave < kWaves / 2 ? Abase : Bbase) + (int64_t)ks * (BKH * 2);
+#pragma unroll
+    for (int i = 0; i < kDmaPerStage; ++i)
+      dma16(src, voff[i], lds_base + stage * kStageBytes + (wave * kDmaPerStage + i) * 1024);
+  };
 
   v4f acc[4][4];
 #pragma unroll
@@ -153,61 +229,68 @@ w4a4_gemm_kernel(int64_t M, int64_t N, int64_t K, const uint8_t* __restrict__ A,
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  uint4 pa[2], pb[2];
-  float2 sa2[2], sb2[2];
-  auto gload = [&](int kb) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int64_t ra = m0 + cr0 + 64 * i, rb = n0 + cr0 + 64 * i;
-      pa[i] = *reinterpret_cast<const uint4*>(A + ra * (K / 2) + (int64_t)kb * 64 + cc * 16);
-      pb[i] = *reinterpret_cast<const uint4*>(B + rb * (K / 2) + (int64_t)kb * 64 + cc * 16);
-      sa2[i] = *reinterpret_cast<const float2*>(SA + ra * ng + (int64_t)kb * 8 + cc * 2);
-      sb2[i] = *reinterpret_cast<const float2*>(SB + rb * ng + (int64_t)kb * 8 + cc * 2);
-    }
-  };
-  auto lstore = [&]() {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int r = cr0 + 64 * i;
-      uint4 h[4];
-      dequant32(pa[i], sa2[i].x, sa2[i].y, h);
-#pragma unroll
-      for (int c = 0; c < 4; ++c)
-        *reinterpret_cast<uint4*>(at + r * kRowBytes + (((cc * 4 + c) ^ swz16(r)) * 16)) = h[c];
-      dequant32(pb[i], sb2[i].x, sb2[i].y, h);
-#pragma unroll
-      for (int c = 0; c < 4; ++c)
-        *reinterpret_cast<uint4*>(bt + r * kRowBytes + (((cc * 4 + c) ^ swz16(r)) * 16)) = h[c];
-    }
-  };
-
-  gload(0);
-  for (int kb = 0; kb < nkb; ++kb) {
-    __syncthreads();           // previous step's LDS reads are done
-    lstore();
+  // fragment reads: lane (l16, q) takes 8 fp16 (K [8q, 8q+8) of the wave's 32-K half kw
+  // of a stage) of rows 16 i + l16 of its A rows and of its B rows; rows 16 apart share a
+  // swizzle key, so each fragment is a lane base plus an immediate
+  const int arow = wm * 64 + l16, brow = wn * 64 + l16;
+  const int a_off = arow * kRowBytes + (((4 * kw + q) ^ swz(arow)) << 4);
+  const int b_off = brow * kRowBytes + (((4 * kw + q) ^ swz(brow)) << 4);
+  auto step = [&](auto st_tag, int ks) {
+    constexpr int ST = decltype(st_tag)::value;
+    // stage ks landed (this wave's DMA; the groups of stages ks+1, ks+2 may fly), then the
+    // barrier makes it true for every wave and proves buffer (ks + 3) % 4 free
+    if (ks + 2 < nks) wait_vmcnt<2 * kDmaPerStage>();
+    else if (ks + 1 < nks) wait_vmcnt<kDmaPerStage>();
+    else wait_vmcnt<0>();
     __syncthreads();
-    if (kb + 1 < nkb) gload(kb + 1);
+    if (ks + 3 < nks) issue(ks + 3, (ST + 3) % kStages);
+    const uint8_t* at = smem + ST * kStageBytes + a_off;
+    const uint8_t* bt = smem + ST * kStageBytes + kTileBytes + b_off;
+    v8h af[4], bf[4];
 #pragma unroll
-    for (int s = 0; s < BK / 32; ++s) {
-      v8h af[4], bf[4];
+    for (int i = 0; i < 4; ++i) af[i] = *reinterpret_cast<const v8h*>(at + 16 * i * kRowBytes);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = wm * 64 + 16 * i + l16;
-        const uint4 v = *reinterpret_cast<const uint4*>(at + r * kRowBytes + (((s * 4 + q) ^ swz16(r)) * 16));
-        af[i] = __builtin_bit_cast(v8h, v);
-      }
+    for (int j = 0; j < 4; ++j) bf[j] = *reinterpret_cast<const v8h*>(bt + 16 * j * kRowBytes);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int r = wn * 64 + 16 * j + l16;
-        const uint4 v = *reinterpret_cast<const uint4*>(bt + r * kRowBytes + (((s * 4 + q) ^ swz16(r)) * 16));
-        bf[j] = __builtin_bit_cast(v8h, v);
-      }
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bf[j], af[i], acc[i][j], 0, 0, 0);
-    }
+      for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bf[j], af[i], acc[i][j], 0, 0, 0);
+  };
+  if (nks > 0) issue(0, 0);
+  if (nks > 1) issue(1, 1);
+  if (nks > 2) issue(2, 2);
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+  for (int ks = 0; ks < nks; ks += 4) {
+    step(I0{}, ks);
+    if (ks + 1 < nks) step(I1{}, ks + 1);
+    if (ks + 2 < nks) step(I2{}, ks + 2);
+    if (ks + 3 < nks) step(I3{}, ks + 3);
   }
+
+  // the two K halves: waves 4-7 hand their sums to waves 0-3 through the (now free) ring
+  __syncthreads();
+  v4f* red = reinterpret_cast<v4f*>(smem);        // [4 quadrants][16 subtiles][64 lanes]
+  if (kw == 1) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) red[((wave & 3) * 16 + 4 * i + j) * 64 + lane] = acc[i][j];
+  }
+  __syncthreads();
+  if (kw == 1) return;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const v4f o = red[((wave & 3) * 16 + 4 * i + j) * 64 + lane];
+      acc[i][j][0] += o[0];
+      acc[i][j][1] += o[1];
+      acc[i][j][2] += o[2];
+      acc[i][j][3] += o[3];
+    }
 
   // low-rank step: acc += T[m][0:32] · L_up[0:32][n]  (one bf16 MFMA K step of 32)
   if (rank == 32) {
@@ -249,27 +332,40 @@ w4a4_gemm_kernel(int64_t M, int64_t N, int64_t K, const uint8_t* __restrict__ A,
   }
 }
 
-// workspace: T [M][32] bf16, then LdT [32][K] bf16 (16-byte aligned)
-size_t w4a4_workspace_bytes(int64_t M, int64_t K, int32_t rank) {
-  if (rank == 0) return 0;
-  return (size_t)(((M * 32 * 2 + 15) / 16) * 16 + 32 * K * 2);
+// workspace: A and B dequantized to fp16 ([M][K], [N][K]), then with the low-rank
+// branch T [M][32] bf16 and LdT [32][K] bf16; every part 256-byte aligned
+namespace {
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+}  // namespace
+
+size_t w4a4_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t rank) {
+  size_t b = align256((size_t)M * K * 2) + align256((size_t)N * K * 2);
+  if (rank > 0) b += align256((size_t)M * 32 * 2) + align256((size_t)32 * K * 2);
+  return b;
 }
 
 hipError_t launch_w4a4(int64_t M, int64_t N, int64_t K, const uint8_t* a, const float* sa,
                        const uint8_t* b, const float* sb, const uint16_t* x_bf16,
                        const uint16_t* l_down, const uint16_t* l_up, int32_t rank,
-                       const uint16_t* bias, uint16_t* d, int64_t ldd, void* ws, hipStream_t st) {
+                       const uint16_t* bias, uint16_t* d, int64_t ldd, void* ws, int num_cus, hipStream_t st) {
   if (M == 0 || N == 0) return hipSuccess;
-  uint16_t* T = reinterpret_cast<uint16_t*>(ws);
-  if (rank > 0) {
-    uint16_t* LdT = reinterpret_cast<uint16_t*>(reinterpret_cast<uint8_t*>(ws) + ((M * 32 * 2 + 15) / 16) * 16);
-    hipLaunchKernelGGL(w4a4_ld_transpose_kernel, dim3((unsigned)((K * 32 + 255) / 256)), dim3(256), 0, st, l_down, K,
-                       LdT);
+  if (M % BM != 0 || N % BN != 0 || K % 128 != 0 || K == 0) return hipErrorInvalidValue;
+  uint8_t* w = reinterpret_cast<uint8_t*>(ws);
+  uint16_t* Ah = reinterpret_cast<uint16_t*>(w);
+  uint16_t* Bh = reinterpret_cast<uint16_t*>(w + align256((size_t)M * K * 2));
+  uint8_t* rest = w + align256((size_t)M * K * 2) + align256((size_t)N * K * 2);
+  (void)num_cus;
+  const int64_t na = M * K / 32, nb = N * K / 32, nld = rank > 0 ? K * 32 : 0;
+  uint16_t* T = reinterpret_cast<uint16_t*>(rest);
+  uint16_t* LdT = reinterpret_cast<uint16_t*>(rest + align256((size_t)M * 32 * 2));
+  const int64_t blocks = (na + 255) / 256 + (nb + 255) / 256 + (nld + 255) / 256;
+  hipLaunchKernelGGL(w4a4_prep_kernel, dim3((unsigned)blocks), dim3(256), 0, st, a, sa, na, Ah, b, sb, nb, Bh,
+                     l_down, nld, rank > 0 ? LdT : nullptr, K);
+  if (rank > 0)
     hipLaunchKernelGGL(w4a4_lowrank_down_kernel, dim3((unsigned)((M + 15) / 16)), dim3(256), 0, st, x_bf16, M, K,
                        LdT, T);
-  }
   const int64_t tiles = (M / BM) * (N / BN);
-  hipLaunchKernelGGL(w4a4_gemm_kernel, dim3((unsigned)tiles), dim3(256), 0, st, M, N, K, a, sa, b, sb,
+  hipLaunchKernelGGL(w4a4_gemm_kernel, dim3((unsigned)tiles), dim3(64 * kWaves), 0, st, M, N, K, Ah, Bh,
                      rank > 0 ? T : nullptr, l_up, (int)rank, bias, d, ldd);
   return hipGetLastError();
 }

@@ -286,12 +286,13 @@ fgg_status fgg_pack_fp4_weights(const void* b, const void* b_scales, int32_t G, 
  *   b [N][K/2], b_scales [N][K/16];
  *   D = bf16( Σ_g16 sA[m,g]·sB[n,g]·Σ_{k in g} A[m][k]·B[n][k]
  *             + (x_bf16 · l_down) · l_up + bias )
- *   The operands are dequantized on chip to fp16 (x·s rounded once) and
- *   contracted with fp16 MFMA in fp32; the rank-32 intermediate
+ *   The operands are dequantized once to fp16 (x·s rounded once) into the
+ *   workspace and contracted with fp16 MFMA in fp32; the rank-32 intermediate
  *   x_bf16 · l_down is accumulated in fp32 (bf16 MFMA) and rounded to bf16.
  *   Requires M % 128 == 0, K % 128 == 0, K >= 128, N % 128 == 0, rank in {0, 32}.
- *   With a low-rank branch, workspace must hold fgg_scaled_gemm_workspace()
- *   bytes (the [M][32] intermediate and a [32][K] transposed copy of l_down).
+ *   workspace (256-byte aligned) must hold fgg_scaled_gemm_workspace() bytes:
+ *   the fp16 copies of A and B, and with a low-rank branch the [M][32]
+ *   intermediate and a [32][K] transposed copy of l_down.  The FP8 case needs none.
  */
 fgg_status fgg_scaled_gemm_workspace(int64_t M, int64_t N, int64_t K, fgg_qdesc aq, fgg_qdesc bq,
                                      const fgg_epilogue* epi, size_t* bytes);

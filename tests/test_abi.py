@@ -113,6 +113,11 @@ def test_gemm_and_permute_reject_bad_arguments_on_host():
     assert lib.fgg_pack_fp4_weights_bytes(1, 40, 384, ctypes.byref(nb), ctypes.byref(ns)) == 2
     assert lib.fgg_pack_fp4_weights(g, g, 1, 32, 200, g, g, None) == 2
     assert lib.fgg_pack_fp4_weights(g, g, 1, 32, 256, ctypes.c_void_p(g.value + 8), g, None) == 1
+    # W4A4 always needs its workspace (the fp16 operand copies)
+    nbytes = ctypes.c_size_t(0)
+    assert lib.fgg_scaled_gemm_workspace(256, 128, 256, W, W, None, ctypes.byref(nbytes)) == 0
+    assert nbytes.value >= 2 * (256 * 256 + 128 * 256)
+    assert lib.fgg_scaled_gemm(256, 128, 256, g, g, W, g, g, W, None, g, 128, None, 0, None) == 1
     # W4A4 with K == 0 is not supported
     assert lib.fgg_scaled_gemm(256, 128, 0, g, g, W, g, g, W, None, g, 128, None, 0, None) == 2
     # permute: bad k / E, missing workspace

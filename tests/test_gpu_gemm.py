@@ -474,6 +474,20 @@ def test_w4a4_small():
     tol_check(y, ref, what="w4a4 small")
 
 
+def test_w4a4_no_epilogue():
+    """No low-rank branch and no bias: the plain W4A4 product."""
+    wl = synth.w4a4(seed=78, M=128, N=256, K=384)
+    M, N, K = 128, 256, 384
+    xq, xs = fgg.quantize_blockwise(cuda(wl["x"]), fgg.Q_E2M1_1x16)
+    wq, ws = fgg.quantize_blockwise(cuda(wl["w"]), fgg.Q_E2M1_1x16)
+    y = to_np(fgg.scaled_gemm(xq, xs, wq, ws, qdesc="w4a4"))
+    qx_r, sx_r = oracle.quantize_e2m1_fp32_groups(wl["x"], 16)
+    qw_r, sw_r = oracle.quantize_e2m1_fp32_groups(wl["w"], 16)
+    assert np.array_equal(to_np(xq), F.pack_e2m1x2(qx_r)) and np.array_equal(to_np(wq), F.pack_e2m1x2(qw_r))
+    ref = oracle.round_bf16(oracle.w4a4_lowrank_gemm(qx_r, sx_r, qw_r, sw_r))
+    tol_check(y, ref, what="w4a4 without epilogue")
+
+
 def test_w4a4_full_size_sampled():
     wl = synth.w4a4()
     y, ref = _w4a4_run(wl, rows=np.array([0, 1, 63, 64, 1000, 2048, 4000, 4095]))
