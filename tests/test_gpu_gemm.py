@@ -173,6 +173,46 @@ def test_k_zero_gives_zeros():
     assert np.all(q[256:] == 0xAB) and np.all(s[:, 256:] == -3.0)
 
 
+def test_grouped_contiguous_max_groups():
+    """1024 experts (the limit), almost all empty, the used ones spread over the
+    whole id range: every tile finds its expert in the workgroup's group table."""
+    G, N, K = 1024, 128, 128
+    counts = [0] * G
+    for e, c in ((0, 3), (1, 130), (511, 1), (512, 128), (1000, 200), (1023, 77)):
+        counts[e] = c
+    x, w, offsets = _contig_case(4242, counts, N, K)
+    xq, xs = fgg.quantize_blockwise(cuda(x), fgg.Q_E4M3_1x128)
+    bq, sb = _quant_weights_gpu(w, fgg.Q_E4M3_128x128)
+    y = to_np(fgg.grouped_gemm_scaled(xq, xs, bq, sb, offsets=cuda(offsets)))
+    yc = to_np(fgg.grouped_gemm_scaled(xq, xs, bq, sb, offsets=cuda(offsets),
+                                       masked_m=cuda(np.array(counts, np.int32))))
+    aq_r, sa_r = oracle.quantize_e4m3_blocks(x, 1, 128)
+    mt = int(offsets[-1])
+    used = [e for e in range(G) if counts[e] > 0]
+    for e in used:
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        bq_r, sb_r = oracle.quantize_e4m3_blocks(w[e], 128, 128)
+        ref = oracle.round_bf16(oracle.grouped_gemm_contiguous(aq_r[lo:hi], sa_r[lo:hi], bq_r[None], sb_r[None],
+                                                               np.array([0, hi - lo])))
+        tol_check(y[lo:hi], ref, what=f"expert {e} of 1024")
+        assert np.array_equal(yc[lo:lo + counts[e]], y[lo:lo + counts[e]])
+    assert mt == sum(-(-c // 128) * 128 for c in counts)
+
+
+def test_grouped_contiguous_max_k():
+    """K = 16384 (the contiguous layout's limit: 128 K blocks)."""
+    counts, N, K = [130, 5], 256, 16384
+    x, w, offsets = _contig_case(99, counts, N, K)
+    xq, xs = fgg.quantize_blockwise(cuda(x), fgg.Q_E4M3_1x128)
+    bq, sb = _quant_weights_gpu(w, fgg.Q_E4M3_128x128)
+    y = to_np(fgg.grouped_gemm_scaled(xq, xs, bq, sb, offsets=cuda(offsets)))
+    aq_r, sa_r = oracle.quantize_e4m3_blocks(x, 1, 128)
+    bq_r, sb_r = _quant_weights_oracle(w)
+    mt = int(offsets[-1])
+    ref = oracle.round_bf16(oracle.grouped_gemm_contiguous(aq_r, sa_r, bq_r, sb_r, offsets))[:mt]
+    tol_check(y[:mt], ref, what="grouped contiguous K=16384")
+
+
 @pytest.mark.parametrize("M,N,K", [(500, 256, 1024), (128, 128, 128), (1, 128, 256)])
 def test_dense_small_and_one_group_identity(M, N, K):
     g = synth.rng(M + N + K)
