@@ -358,8 +358,12 @@ def main():
             "frac": round(gu_tf / PEAK_FP8_TFLOPS, 4),
             "traffic": measured_traffic(os.path.dirname(os.path.abspath(__file__))),
             "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE x2 + WRITE_SIZE, copy-calibrated)",
-            "algorithmic": "2*8192*4096*7168 = %.1f GFLOP per launch; A+B+D = %.0f MB" % (
-                gu_flops / 1e9, (m_total * cfg["K"] + cfg["E"] * cfg["N_gu"] * cfg["K"] + 2 * m_total * cfg["N_gu"]) / 1e6),
+            "algorithmic": ("2*8192*4096*7168 = %.1f GFLOP per launch; bytes: A codes + scales, B codes + scales, "
+                            "output codes + scales of the routed rows = %.0f MB") % (
+                gu_flops / 1e9,
+                (m_total * cfg["K"] * (1 + 4 / 128)
+                 + cfg["E"] * cfg["N_gu"] * cfg["K"] * (1 + 4 / (128 * 128))
+                 + cfg["T"] * cfg["k"] * cfg["E"] // cfg["E_global"] * (cfg["N_gu"] // 2) * (1 + 4 / 128)) / 1e6),
         },
     }
     if not args.no_secondary:
