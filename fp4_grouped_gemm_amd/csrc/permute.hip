@@ -265,7 +265,7 @@ __global__ void __launch_bounds__(256) permute_quantize_kernel(const int32_t* __
                                                                 int64_t T, int64_t K,
                                                                 uint8_t* __restrict__ a_out,
                                                                 float* __restrict__ sa_out, int64_t M_cap) {
-  constexpr int kPB = 4;   // passes of 1024 columns loaded together
+  constexpr int kPB = 2;   // passes of 1024 columns loaded together
   const int lane = threadIdx.x & 63, sub = lane & 7;
   const int64_t wave_id = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int64_t nwaves = (int64_t)gridDim.x * 4;
