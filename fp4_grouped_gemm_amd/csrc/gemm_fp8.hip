@@ -19,7 +19,8 @@
 //  * the weight tile is the MFMA's first operand, so every lane's four outputs
 //    are four consecutive columns of one row: one sA per lane per 16-row
 //    subtile, one sB per wave (a wave's 64 columns lie in one 128-column scale
-//    block), and 8-byte bf16 stores.
+//    block; two in the SiLU instance, whose waves hold gate and up columns),
+//    and 8-byte bf16 stores.
 //  * grouped kernel: workgroup tile 128 x 256: 8 waves of 64 x 64 (4 x 4 MFMA subtiles, 64 fp32
 //    accumulators per lane), two waves per SIMD so that one wave's MFMAs
 //    overlap the other's promotion FMAs, LDS reads and barrier waits; one
@@ -33,17 +34,19 @@
 //    is counted by hand with s_waitcnt vmcnt, because the compiler's own wait
 //    insertion cannot tell which stage a read depends on and would drain the
 //    whole ring before every read.  No other vector-memory instruction is
-//    issued inside the K loop (scale sB comes through the scalar cache), so
-//    each wave's vmcnt counts exactly its own DMA instructions.
+//    issued inside the K loop (the weight scales ride along with each stage's
+//    DMA), so each wave's vmcnt counts exactly its own DMA instructions.
 //  * LDS rows are 128 B; the 16-byte chunk c of row r lives at chunk
-//    c ^ ((r ^ (r >> 3)) & 7) (realized by choosing each lane's source
-//    address, since a DMA instruction writes 1 KB contiguously), keeping the
-//    16-row operand reads free of bank conflicts for 32 and 64 banks.
+//    c ^ swz(r), swz(r) = (r & 7) ^ ((r >> 3) & 1) (realized by choosing each
+//    lane's source address, since a DMA instruction writes 1 KB contiguously),
+//    keeping the 16-row operand reads free of bank conflicts.
 //  * persistent grid (one workgroup per CU), XCD-aware: each XCD's workgroups
 //    take one super-tile of 8 x 4 output tiles per round, so the A and B blocks
 //    they share are fetched once into that XCD's L2; a tile's expert is found
-//    by binary search over the segment offsets (segments are multiples of 128
-//    rows, so a tile never straddles two experts).
+//    by binary search over the workgroup's LDS copy of the segment offsets
+//    (segments are multiples of 128 rows, so a tile never straddles two
+//    experts), and with per-expert row counts, tiles and 64-row halves that hold
+//    only padding are skipped.
 #include <type_traits>
 
 #include "fgg_device.hpp"
