@@ -267,7 +267,8 @@ fgg_status fgg_scaled_gemm(int64_t M, int64_t N, int64_t K, const void* a, const
                                               (uint16_t*)d, ldd, num_cus, (hipStream_t)stream));
   }
   if (same_q(aq, FGG_E2M1X2, FGG_F32, 1, 16) && same_q(bq, FGG_E2M1X2, FGG_F32, 1, 16)) {
-    if (M % 128 != 0 || K == 0) return FGG_ERR_UNSUPPORTED;
+    // (the GEMM's per-lane DMA offsets are 32-bit: 128 rows x 2K bytes)
+    if (M % 128 != 0 || K == 0 || K > (int64_t(1) << 22)) return FGG_ERR_UNSUPPORTED;
     if (!aligned(a_scales, 8) || !aligned(b_scales, 8)) return FGG_ERR_INVALID_VALUE;
     const int32_t rank = epi ? epi->rank : 0;
     if (rank != 0 && rank != 32) return FGG_ERR_UNSUPPORTED;

@@ -382,7 +382,7 @@ hipError_t launch_gemm_masked(bool b_fp4, bool tiled, int32_t G, int64_t M, int6
 //   scales: span (g, n/16, j/16) is 256 bytes; bytes [16 r, 16 r + 16) are row
 //          16(n/16) + r's scale bytes [16 (j/16), 16 (j/16) + 16), 127 past K/32
 __global__ void __launch_bounds__(256)
-pack_fp4_tiles_kernel(const uint8_t* __restrict__ b, uint8_t* __restrict__ bt, int64_t pieces, int64_t N, int64_t K) {
+pack_fp4_tiles_kernel(const uint8_t* __restrict__ b, uint8_t* __restrict__ bt, int64_t pieces, int64_t K) {
   const int64_t nkb = K / 128;
   for (int64_t p = (int64_t)blockIdx.x * 256 + threadIdx.x; p < pieces; p += (int64_t)gridDim.x * 256) {
     const int lane = (int)(p & 63);
@@ -396,7 +396,7 @@ pack_fp4_tiles_kernel(const uint8_t* __restrict__ b, uint8_t* __restrict__ bt, i
 
 __global__ void __launch_bounds__(256)
 pack_fp4_scale_tiles_kernel(const uint8_t* __restrict__ s, uint8_t* __restrict__ st, int64_t rows_spans,
-                            int64_t N, int64_t K) {
+                            int64_t K) {
   const int64_t nsc = K / 32, nspan = (nsc + 15) / 16;
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < rows_spans; i += (int64_t)gridDim.x * 256) {
     // i = ((g * N/16 + nb) * nspan + span) * 16 + r
@@ -430,8 +430,8 @@ hipError_t launch_pack_fp4(int32_t G, int64_t N, int64_t K, const uint8_t* b, co
   int64_t g1 = (pieces + 255) / 256, g2 = (rows_spans + 255) / 256;
   if (g1 > cap) g1 = cap;
   if (g2 > cap) g2 = cap;
-  hipLaunchKernelGGL(pack_fp4_tiles_kernel, dim3((unsigned)g1), dim3(256), 0, stream, b, bt, pieces, N, K);
-  hipLaunchKernelGGL(pack_fp4_scale_tiles_kernel, dim3((unsigned)g2), dim3(256), 0, stream, s, st, rows_spans, N, K);
+  hipLaunchKernelGGL(pack_fp4_tiles_kernel, dim3((unsigned)g1), dim3(256), 0, stream, b, bt, pieces, K);
+  hipLaunchKernelGGL(pack_fp4_scale_tiles_kernel, dim3((unsigned)g2), dim3(256), 0, stream, s, st, rows_spans, K);
   return hipGetLastError();
 }
 

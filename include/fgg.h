@@ -289,7 +289,7 @@ fgg_status fgg_pack_fp4_weights(const void* b, const void* b_scales, int32_t G, 
  *   The operands are dequantized once to fp16 (x·s rounded once) into the
  *   workspace and contracted with fp16 MFMA in fp32; the rank-32 intermediate
  *   x_bf16 · l_down is accumulated in fp32 (bf16 MFMA) and rounded to bf16.
- *   Requires M % 128 == 0, K % 128 == 0, K >= 128, N % 128 == 0, rank in {0, 32}.
+ *   Requires M % 128 == 0, K % 128 == 0, 128 <= K <= 2^22, N % 128 == 0, rank in {0, 32}.
  *   workspace (256-byte aligned) must hold fgg_scaled_gemm_workspace() bytes:
  *   the fp16 copies of A and B, and with a low-rank branch the [M][32]
  *   intermediate and a [32][K] transposed copy of l_down.  The FP8 case needs none.
