@@ -20,8 +20,9 @@
 // and one of the two 32-wide halves of every K stage (two waves per SIMD; the two
 // halves' fp32 sums are added through LDS at the end); a 4-buffer LDS ring of
 // 64-wide K stages (A and B, 2 x 128 rows x 128 bytes of fp16 = 32 KB each)
-// filled by global_load_lds_dwordx4 with three stages in flight; each 128-byte
-// row's 16-byte chunks XOR-swizzled by the row index.
+// filled by global_load_lds_dwordx4 with up to three stages in flight, the next
+// stage's fragments read into registers while the current stage's MFMAs run; each
+// 128-byte row's 16-byte chunks XOR-swizzled by the row index.
 #include <algorithm>
 #include <type_traits>
 
@@ -235,39 +236,58 @@ w4a4_gemm_kernel(int64_t M, int64_t N, int64_t K, const uint16_t* __restrict__ A
   const int arow = wm * 64 + l16, brow = wn * 64 + l16;
   const int a_off = arow * kRowBytes + (((4 * kw + q) ^ swz(arow)) << 4);
   const int b_off = brow * kRowBytes + (((4 * kw + q) ^ swz(brow)) << 4);
-  auto step = [&](auto st_tag, int ks) {
-    constexpr int ST = decltype(st_tag)::value;
-    // stage ks landed (this wave's DMA; the groups of stages ks+1, ks+2 may fly), then the
-    // barrier makes it true for every wave and proves buffer (ks + 3) % 4 free
-    if (ks + 2 < nks) wait_vmcnt<2 * kDmaPerStage>();
-    else if (ks + 1 < nks) wait_vmcnt<kDmaPerStage>();
+  // One stage: the MFMAs of stage ks run on fragments already in registers while the
+  // fragments of stage ks + 1 are read from LDS (two register sets in rotation).
+  //   top of step ks: this wave's DMA of stage ks + 1 done (the groups of stages ks + 2,
+  //   ks + 3 may fly), its reads of stage ks done; the barrier makes both true for every
+  //   wave, so buffer ks % 4 is free and takes stage ks + 4.
+  struct Frags {
+    v8h a[4], b[4];
+  };
+  auto read_frags = [&](int slot, Frags& f) {
+    const uint8_t* at = smem + slot * kStageBytes + a_off;
+    const uint8_t* bt = smem + slot * kStageBytes + kTileBytes + b_off;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) f.a[i] = *reinterpret_cast<const v8h*>(at + 16 * i * kRowBytes);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) f.b[j] = *reinterpret_cast<const v8h*>(bt + 16 * j * kRowBytes);
+  };
+  auto step = [&](auto st_tag, int ks, const Frags& cur, Frags& nxt) {
+    constexpr int ST = decltype(st_tag)::value;     // == ks % 4
+    const int after = nks - 2 - ks;                 // stages issued after stage ks + 1
+    if (after >= 2) wait_vmcnt<2 * kDmaPerStage>();
+    else if (after == 1) wait_vmcnt<kDmaPerStage>();
     else wait_vmcnt<0>();
     __syncthreads();
-    if (ks + 3 < nks) issue(ks + 3, (ST + 3) % kStages);
-    const uint8_t* at = smem + ST * kStageBytes + a_off;
-    const uint8_t* bt = smem + ST * kStageBytes + kTileBytes + b_off;
-    v8h af[4], bf[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) af[i] = *reinterpret_cast<const v8h*>(at + 16 * i * kRowBytes);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) bf[j] = *reinterpret_cast<const v8h*>(bt + 16 * j * kRowBytes);
+    if (ks + 4 < nks) issue(ks + 4, ST);
+    if (ks + 1 < nks) read_frags((ST + 1) % kStages, nxt);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bf[j], af[i], acc[i][j], 0, 0, 0);
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(cur.b[j], cur.a[i], acc[i][j], 0, 0, 0);
   };
   if (nks > 0) issue(0, 0);
   if (nks > 1) issue(1, 1);
   if (nks > 2) issue(2, 2);
+  if (nks > 3) issue(3, 3);
+  // stage 0 landed (three groups may fly)
+  if (nks > 3) wait_vmcnt<3 * kDmaPerStage>();
+  else if (nks > 2) wait_vmcnt<2 * kDmaPerStage>();
+  else if (nks > 1) wait_vmcnt<kDmaPerStage>();
+  else wait_vmcnt<0>();
+  __syncthreads();
+  Frags f0, f1;
+  if (nks > 0) read_frags(0, f0);
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;
   using I3 = std::integral_constant<int, 3>;
   for (int ks = 0; ks < nks; ks += 4) {
-    step(I0{}, ks);
-    if (ks + 1 < nks) step(I1{}, ks + 1);
-    if (ks + 2 < nks) step(I2{}, ks + 2);
-    if (ks + 3 < nks) step(I3{}, ks + 3);
+    step(I0{}, ks, f0, f1);
+    if (ks + 1 < nks) step(I1{}, ks + 1, f1, f0);
+    if (ks + 2 < nks) step(I2{}, ks + 2, f0, f1);
+    if (ks + 3 < nks) step(I3{}, ks + 3, f1, f0);
   }
 
   // the two K halves: waves 4-7 hand their sums to waves 0-3 through the (now free) ring
