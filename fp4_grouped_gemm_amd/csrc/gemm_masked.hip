@@ -195,6 +195,13 @@ gemm_masked_v2_kernel(int G, int64_t M, int64_t N, int64_t K, const uint8_t* __r
 // (rows padded by 16 bytes so that the MFMA-layout 16-byte reads of any 16
 // lanes with equal q hit distinct banks); the next chunk's global loads are in
 // flight during the current chunk, and one barrier per chunk publishes it.
+// 16 bytes at p (16-byte aligned) with the nontemporal (streaming) cache policy.
+__device__ inline uint4 load_stream16(const uint8_t* p) {
+  typedef unsigned v4u __attribute__((ext_vector_type(4)));
+  const v4u v = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 template <int UA>
 struct MaskedLds {
   static constexpr int kRowBytes = UA * 128 + 16;
@@ -277,17 +284,20 @@ gemm_masked_fp4_lds_kernel(int G, int64_t M, int64_t N, int64_t K, const uint8_t
     uint4 b[U];
     uint32_t sc[U];
   };
+  // Weight bytes are read exactly once: nontemporal loads (streaming cache policy) keep
+  // them from displacing the activations, which every workgroup of a group re-reads
+  // (measured: 87.5-90 us -> 81.5 us for the 499 MB decode stream).
   auto load_b = [&](BStage& st, int step) {
     const int kb0 = step * U;
 #pragma unroll
     for (int u = 0; u < U; ++u)
-      if (kb0 + u < nkb) st.b[u] = *reinterpret_cast<const uint4*>(Br + (int64_t)(kb0 + u) * kBStride);
+      if (kb0 + u < nkb) st.b[u] = load_stream16(Br + (int64_t)(kb0 + u) * kBStride);
 #pragma unroll
     for (int u4 = 0; u4 < U / 4; ++u4) {
       const int kb = kb0 + 4 * u4;
       const uint8_t* sr = Sr + (int64_t)(kb / 4) * kSStride;
       if (TILED || kb + 4 <= nkb) {         // (a tiled span is always 16 bytes, padded with 2^0)
-        const uint4 v = *reinterpret_cast<const uint4*>(sr);
+        const uint4 v = load_stream16(sr);
         st.sc[4 * u4 + 0] = v.x; st.sc[4 * u4 + 1] = v.y; st.sc[4 * u4 + 2] = v.z; st.sc[4 * u4 + 3] = v.w;
       } else {
 #pragma unroll
