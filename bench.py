@@ -55,27 +55,72 @@ def _sync():
     torch.cuda.synchronize()
 
 
-class EventTimer:
-    """Accumulates the device time of one launch site, with HIP events recorded on
-    the current stream (the stream the library's kernels are enqueued on).  The
-    events are created before the timed loop: creating them inside it added tens
-    of microseconds per step."""
+HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000   # hipEventDisableSystemFence (hip_runtime_api.h)
 
-    def __init__(self, n):
+
+def _hip_runtime():
+    """The HIP runtime library torch has loaded (the one the library's kernels run on)."""
+    import ctypes
+    import torch  # noqa: F401  (loads the runtime)
+    path = next((l.split()[-1] for l in open("/proc/self/maps") if "libamdhip64" in l), "libamdhip64.so")
+    hip = ctypes.CDLL(path)
+    P = ctypes.c_void_p
+    hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(P), ctypes.c_uint]
+    hip.hipEventRecord.argtypes = [P, P]
+    hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), P, P]
+    hip.hipEventDestroy.argtypes = [P]
+    return hip
+
+
+class StepMarks:
+    """HIP events at fixed points of every timed step, recorded on the current stream
+    (the stream the library's kernels are enqueued on): before the gate-up GEMM,
+    between the two GEMMs (one event ends the gate-up interval and starts the down
+    interval) and after the down GEMM.  Every event recorded between two kernels
+    leaves a gap of a few microseconds in the step (kernel trace), so there are as
+    few as the two intervals need.  The events are created before the timed loop
+    (creating them inside it added tens of microseconds per step) and without the
+    system-scope fence (with it, the gap per event was ~5.7 us and the following
+    kernel started with the L2 written back)."""
+
+    def __init__(self, steps, marks=3):
+        import ctypes
         import torch
-        self.events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                       for _ in range(n)]
-        self.used = 0
+        self.hip = _hip_runtime()
+        self.stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        self.events = []
+        for _ in range(steps):
+            row = tuple(ctypes.c_void_p() for _ in range(marks))
+            for ev in row:
+                if self.hip.hipEventCreateWithFlags(ctypes.byref(ev), HIP_EVENT_DISABLE_SYSTEM_FENCE) != 0:
+                    raise RuntimeError("hipEventCreateWithFlags failed")
+            self.events.append(row)
+        self.step = 0
 
-    def start(self):
-        self.events[self.used][0].record()
+    def mark(self, i):
+        if self.hip.hipEventRecord(self.events[self.step][i], self.stream) != 0:
+            raise RuntimeError("hipEventRecord failed")
 
-    def stop(self):
-        self.events[self.used][1].record()
-        self.used += 1
+    def next_step(self):
+        self.step += 1
 
-    def mean_ms(self):
-        return float(np.mean([a.elapsed_time(b) for a, b in self.events[:self.used]])) if self.used else float("nan")
+    def mean_ms(self, i, j):
+        """Mean over the recorded steps of the time from mark i to mark j (call after the
+        stream has been synchronized)."""
+        import ctypes
+        ms = []
+        for row in self.events[:self.step]:
+            t = ctypes.c_float()
+            if self.hip.hipEventElapsedTime(ctypes.byref(t), row[i], row[j]) != 0:
+                raise RuntimeError("hipEventElapsedTime failed")
+            ms.append(t.value)
+        return float(np.mean(ms)) if ms else float("nan")
+
+    def close(self):
+        for row in self.events:
+            for ev in row:
+                self.hip.hipEventDestroy(ev)
+        self.events = []
 
 
 # ----------------------------------------------------------------- prefill
@@ -111,24 +156,23 @@ def setup_prefill(fgg, synth, torch):
                 bufs=bufs, useful_flops=useful, routing=r)
 
 
-def prefill_step(fgg, st, t_gu=None, t_dn=None):
+def prefill_step(fgg, st, marks=None):
     b, p = st["bufs"], st["perm"]
     E = st["cfg"]["E"]
     fgg.moe_permute(st["ids"], E, 128, x=st["x"], out=p)       # 1x128 e4m3 quantization fused in
-    if t_gu:
-        t_gu.start()
+    if marks:
+        marks.mark(0)
     # gate-up grouped GEMM with SiLU(gate)*up and the 1x128 e4m3 requantization in its epilogue
     # (the permute's counts let both GEMMs skip the padding rows of each expert segment)
     fgg.grouped_gemm_silu_quantize(p["a"], p["sa"], st["gu_q"], st["gu_s"], p["offsets"], counts=p["counts"],
                                    out=b["a2"], scales=b["s2"])
-    if t_gu:
-        t_gu.stop()
-    if t_dn:
-        t_dn.start()
+    if marks:
+        marks.mark(1)
     fgg.grouped_gemm_scaled(b["a2"], b["s2"], st["dn_q"], st["dn_s"], offsets=p["offsets"], masked_m=p["counts"],
                             out=b["y"])
-    if t_dn:
-        t_dn.stop()
+    if marks:
+        marks.mark(2)
+        marks.next_step()
     fgg.moe_combine(b["y"], p["src_to_row"], st["tw"], out=b["out"])
 
 
@@ -302,14 +346,15 @@ def main():
     for _ in range(args.warmup):
         prefill_step(fgg, st)
     _sync()
-    t_gu, t_dn = EventTimer(args.steps), EventTimer(args.steps)
+    marks = StepMarks(args.steps)
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        prefill_step(fgg, st, t_gu, t_dn)
+        prefill_step(fgg, st, marks)
     _sync()
     wall = time.perf_counter() - t0
     ms_step = wall * 1e3 / args.steps
-    gu_ms, dn_ms = t_gu.mean_ms(), t_dn.mean_ms()
+    gu_ms, dn_ms = marks.mean_ms(0, 1), marks.mean_ms(1, 2)
+    marks.close()
 
     useful = st["useful_flops"]
     value = useful / (ms_step * 1e-3) / 1e12
