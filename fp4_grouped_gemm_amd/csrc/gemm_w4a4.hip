@@ -16,13 +16,12 @@
 // first) and one extra bf16 MFMA step T·L_up per output tile, before the bias
 // is added in the epilogue.
 //
-// GEMM tile: 128 x 128 per 512-thread workgroup: 8 waves, each a 64 x 64 quadrant
-// and one of the two 32-wide halves of every K stage (two waves per SIMD; the two
-// halves' fp32 sums are added through LDS at the end); a 4-buffer LDS ring of
-// 64-wide K stages (A and B, 2 x 128 rows x 128 bytes of fp16 = 32 KB each)
-// filled by global_load_lds_dwordx4 with up to three stages in flight, the next
-// stage's fragments read into registers while the current stage's MFMAs run; each
-// 128-byte row's 16-byte chunks XOR-swizzled by the row index.
+// GEMM tile: 256 x 192 per 256-thread workgroup, one wave per SIMD, each wave 128 x 96
+// outputs with its 192 fp32 accumulators in the accumulation registers; a 4-buffer LDS
+// ring of 32-wide K stages filled by global_load_lds_dwordx4 two stages ahead, the next
+// stage's fragments read into registers while the current stage's MFMAs run (details at
+// the kernel).  Measured on MI355X, v_mfma_f32_16x16x32_f16 issues at about 1.3 PFLOP/s
+// when fed from registers only (half the 2.5 PFLOP/s fp16 figure), which bounds this path.
 #include <algorithm>
 #include <type_traits>
 
@@ -34,15 +33,6 @@ namespace fgg {
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 
 namespace {
-constexpr int BM = 128, BN = 128;
-constexpr int BKH = 64;                       // K elements per LDS stage
-constexpr int kRowBytes = BKH * 2;            // one fp16 row of a stage: 128 bytes
-constexpr int kTileBytes = BM * kRowBytes;    // 16 KB (A or B)
-constexpr int kStageBytes = 2 * kTileBytes;   // A then B
-constexpr int kStages = 4;
-constexpr int kWaves = 8;                     // 2 x 2 output quadrants x 2 halves of each K stage
-constexpr int kDmaPerStage = kStageBytes / 1024 / kWaves;   // 1 KB DMA instructions per wave per stage
-
 __device__ inline float e2m1_f32(uint32_t nib, float s) {
   const uint32_t mag = nib & 7u;
   float f = __uint_as_float((mag + 252u) << 22);        // exact for magnitude codes >= 2
@@ -71,10 +61,6 @@ __device__ inline void dequant32(uint4 packed, float s0, float s1, uint4* out4) 
   out4[2] = make_uint4(h[8], h[9], h[10], h[11]);
   out4[3] = make_uint4(h[12], h[13], h[14], h[15]);
 }
-
-// 16-byte chunk swizzle of a 128-byte row (as in the FP8 GEMM): rows 16 apart share a
-// key; any 8 consecutive rows get 8 distinct keys
-__device__ inline int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 
 __device__ inline void dma16(const void* sbase, uint32_t voff, uint32_t lds) {
   uint32_t save;
@@ -189,96 +175,138 @@ __global__ void __launch_bounds__(256) w4a4_lowrank_down_kernel(const uint16_t* 
                                                  (uint32_t)bf16_bits_rne(s1[2]) | ((uint32_t)bf16_bits_rne(s1[3]) << 16));
 }
 
-__global__ void __launch_bounds__(512, 1)
+// The fp16 GEMM D = A_h · B_hᵀ (+ T · L_up) (+ bias), bf16 out.  Workgroup tile 256 x 192,
+// four waves (one per SIMD), each 128 x 96 outputs: 8 x 6 MFMA subtiles, 192 fp32
+// accumulators per lane, which the matrix core keeps in the accumulation registers (no
+// per-block promotion here, unlike the FP8 path), so a wave's fragments are reused by 6
+// (A) and 8 (B) MFMAs: 299 bytes of LDS reads per MFMA instead of 512 with 64 x 64
+// wave tiles.  The 4096 x 3072 shape is exactly 256 tiles, one per CU.
+// K stages of 32 (one MFMA step): 256 A rows + 192 B rows of 64 bytes = 28 KB, a
+// 4-buffer ring filled by global_load_lds_dwordx4 (7 DMA instructions per wave per
+// stage) two stages ahead; the next stage's fragments are read while the current
+// stage's 48 MFMAs run.  A 64-byte row's four 16-byte chunks are XOR-swizzled with
+// (row >> 2) & 3, so the 16 lanes of one quarter-wave (16 rows, one chunk index) hit
+// 16 distinct bank groups.  Rows past M or N read the last valid row (never stored).
+namespace w4 {
+constexpr int BM = 256, BN = 192, BK = 32;
+constexpr int kRowBytes = BK * 2;                 // 64
+constexpr int kABytes = BM * kRowBytes;           // 16 KB
+constexpr int kStageBytes = (BM + BN) * kRowBytes;  // 28 KB
+constexpr int kStages = 4;
+constexpr int kWaves = 4;
+constexpr int kDma = kStageBytes / 1024 / kWaves; // 7
+constexpr int kAGroups = kABytes / 1024;          // 16 (16 rows per KB)
+constexpr int kGM = 4;                            // tile rows per raster group
+static_assert(kStages * kStageBytes <= 160 * 1024, "LDS budget");
+__device__ inline int key(int row) { return (row >> 2) & 3; }
+}  // namespace w4
+
+__global__ void __launch_bounds__(256, 1)
 w4a4_gemm_kernel(int64_t M, int64_t N, int64_t K, const uint16_t* __restrict__ Ah, const uint16_t* __restrict__ Bh,
                  const uint16_t* __restrict__ T, const uint16_t* __restrict__ Lu, int rank,
                  const uint16_t* __restrict__ bias, uint16_t* __restrict__ D, int64_t ldd) {
+  using namespace w4;
   __shared__ __align__(16) uint8_t smem[kStages * kStageBytes];
   const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave & 1, wn = (wave >> 1) & 1, kw = wave >> 2;
+  const int wm = wave & 1, wn = wave >> 1;
   const int l16 = lane & 15, q = lane >> 4;
-  const int64_t n_tiles = N / BN;
-  const int64_t m0 = (blockIdx.x / n_tiles) * BM, n0 = (blockIdx.x % n_tiles) * BN;
-  const int nks = (int)(K / BKH);
 
-  // DMA roles: a stage is 32 segments of 1 KB (8 rows of 128 bytes): segments 0-15 the A
-  // rows, 16-31 the B rows; wave w issues segments 4w .. 4w+3.  Lane l fills chunk l % 8 of
-  // row l / 8 of its segment and reads source chunk (l % 8) ^ swz(row).
-  const int lrow = lane >> 3;
+  // Tile order: consecutive tile indices go to one XCD (workgroup b runs on XCD b % 8),
+  // rastered in groups of kGM tile rows, so an XCD's tiles share A and B blocks in its L2.
+  const int64_t nM = (M + BM - 1) / BM, nN = (N + BN - 1) / BN, tiles = nM * nN;
+  const int64_t per_xcd = (tiles + 7) / 8;
+  const int64_t t = (int64_t)(blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+  if (t >= tiles) return;
+  const int64_t group = t / (kGM * nN), first_m = group * kGM;
+  const int64_t gm = (nM - first_m) < kGM ? (nM - first_m) : kGM;
+  const int64_t idx = t - group * kGM * nN;
+  const int64_t m0 = (first_m + idx % gm) * BM, n0 = (idx / gm) * BN;
+  const int rows = (int)((M - m0) < BM ? (M - m0) : BM), cols = (int)((N - n0) < BN ? (N - n0) : BN);
+  const bool live = (wm * 128 < rows) && (wn * 96 < cols);
+  const int nks = (int)(K / BK);
+
+  // DMA roles: a stage is 28 segments of 1 KB (16 rows of 64 bytes), segments 0-15 the A
+  // rows, 16-27 the B rows; wave w issues segments 7w .. 7w+6.  Lane l fills chunk l % 4
+  // of row l / 4 of its segment and reads source chunk (l % 4) ^ key(row).
   const uint8_t* Abase = reinterpret_cast<const uint8_t*>(Ah + m0 * K);
   const uint8_t* Bbase = reinterpret_cast<const uint8_t*>(Bh + n0 * K);
-  uint32_t voff[kDmaPerStage];
+  uint32_t voff[kDma];
 #pragma unroll
-  for (int i = 0; i < kDmaPerStage; ++i) {
-    const int seg = (wave * kDmaPerStage + i) & 15;
-    const int row = seg * 8 + lrow;
-    voff[i] = (uint32_t)row * (uint32_t)(K * 2) + (uint32_t)((((lane & 7) ^ swz(row))) * 16);
+  for (int i = 0; i < kDma; ++i) {
+    const int seg = wave * kDma + i;
+    const int row = seg * 16 + (lane >> 2);          // row of the stage ([A rows][B rows])
+    int src = seg < kAGroups ? row : row - BM;
+    const int lim = seg < kAGroups ? rows : cols;
+    if (src >= lim) src = lim - 1;
+    voff[i] = (uint32_t)src * (uint32_t)(K * 2) + (uint32_t)((((lane & 3) ^ key(row))) * 16);
   }
   auto issue = [&](int ks, int stage) {
-    const uint8_t* src = (wave < kWaves / 2 ? Abase : Bbase) + (int64_t)ks * (BKH * 2);
 #pragma unroll
-    for (int i = 0; i < kDmaPerStage; ++i)
-      dma16(src, voff[i], lds_base + stage * kStageBytes + (wave * kDmaPerStage + i) * 1024);
+    for (int i = 0; i < kDma; ++i) {
+      const int seg = wave * kDma + i;               // wave-uniform
+      const uint8_t* src = (seg < kAGroups ? Abase : Bbase) + (int64_t)ks * (BK * 2);
+      dma16(src, voff[i], lds_base + stage * kStageBytes + seg * 1024);
+    }
   };
 
-  v4f acc[4][4];
+  v4f acc[8][6];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 8; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < 6; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  // fragment reads: lane (l16, q) takes 8 fp16 (K [8q, 8q+8) of the wave's 32-K half kw
-  // of a stage) of rows 16 i + l16 of its A rows and of its B rows; rows 16 apart share a
-  // swizzle key, so each fragment is a lane base plus an immediate
-  const int arow = wm * 64 + l16, brow = wn * 64 + l16;
-  const int a_off = arow * kRowBytes + (((4 * kw + q) ^ swz(arow)) << 4);
-  const int b_off = brow * kRowBytes + (((4 * kw + q) ^ swz(brow)) << 4);
-  // One stage: the MFMAs of stage ks run on fragments already in registers while the
-  // fragments of stage ks + 1 are read from LDS (two register sets in rotation).
-  //   top of step ks: this wave's DMA of stage ks + 1 done (the groups of stages ks + 2,
-  //   ks + 3 may fly), its reads of stage ks done; the barrier makes both true for every
-  //   wave, so buffer ks % 4 is free and takes stage ks + 4.
+  // fragments: lane (l16, q) takes 8 fp16 (K [8q, 8q+8) of the stage) of rows 16 i + l16
+  // of the wave's A rows and of its B rows; rows 16 apart share a swizzle key
+  const int arow = wm * 128 + l16, brow = BM + wn * 96 + l16;
+  const int a_off = arow * kRowBytes + ((q ^ key(arow)) << 4);
+  const int b_off = brow * kRowBytes + ((q ^ key(brow)) << 4);
   struct Frags {
-    v8h a[4], b[4];
+    v8h a[8], b[6];
   };
   auto read_frags = [&](int slot, Frags& f) {
-    const uint8_t* at = smem + slot * kStageBytes + a_off;
-    const uint8_t* bt = smem + slot * kStageBytes + kTileBytes + b_off;
+    const uint8_t* base = smem + slot * kStageBytes;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) f.a[i] = *reinterpret_cast<const v8h*>(at + 16 * i * kRowBytes);
+    for (int i = 0; i < 8; ++i) f.a[i] = *reinterpret_cast<const v8h*>(base + a_off + 16 * i * kRowBytes);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) f.b[j] = *reinterpret_cast<const v8h*>(bt + 16 * j * kRowBytes);
+    for (int j = 0; j < 6; ++j) f.b[j] = *reinterpret_cast<const v8h*>(base + b_off + 16 * j * kRowBytes);
   };
+  // top of step ks: this wave's reads of stage ks done and its DMA of stage ks + 1 landed
+  // (stage ks + 2 may fly); the barrier makes both true for every wave, so stage ks + 1
+  // is readable and the buffer of stage ks - 1 is free for stage ks + 3.
   auto step = [&](auto st_tag, int ks, const Frags& cur, Frags& nxt) {
-    constexpr int ST = decltype(st_tag)::value;     // == ks % 4
-    const int after = nks - 2 - ks;                 // stages issued after stage ks + 1
-    if (after >= 2) wait_vmcnt<2 * kDmaPerStage>();
-    else if (after == 1) wait_vmcnt<kDmaPerStage>();
+    constexpr int ST = decltype(st_tag)::value;     // == ks % kStages
+    __builtin_amdgcn_s_waitcnt(0xC07F);             // lgkmcnt(0)
+    // stages issued after stage ks + 1 (up to ks + kStages - 2) may still fly
+    const int last = (ks + kStages - 2) < (nks - 1) ? (ks + kStages - 2) : (nks - 1);
+    const int after = last - (ks + 1);
+    if (after >= 2) wait_vmcnt<2 * kDma>();
+    else if (after == 1) wait_vmcnt<kDma>();
     else wait_vmcnt<0>();
     __syncthreads();
-    if (ks + 4 < nks) issue(ks + 4, ST);
-    if (ks + 1 < nks) read_frags((ST + 1) % kStages, nxt);
+    if (ks + kStages - 1 < nks) issue(ks + kStages - 1, (ST + kStages - 1) % kStages);
+    if (live) {
+      if (ks + 1 < nks) read_frags((ST + 1) % kStages, nxt);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 8; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(cur.b[j], cur.a[i], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < 6; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(cur.b[j], cur.a[i], acc[i][j], 0, 0, 0);
+    }
   };
+  static_assert(kStages == 4, "the prologue and the unrolled loop below assume a 4-buffer ring");
   if (nks > 0) issue(0, 0);
   if (nks > 1) issue(1, 1);
   if (nks > 2) issue(2, 2);
-  if (nks > 3) issue(3, 3);
-  // stage 0 landed (three groups may fly)
-  if (nks > 3) wait_vmcnt<3 * kDmaPerStage>();
-  else if (nks > 2) wait_vmcnt<2 * kDmaPerStage>();
-  else if (nks > 1) wait_vmcnt<kDmaPerStage>();
+  // stage 0 landed (two stages may fly)
+  if (nks > 2) wait_vmcnt<2 * kDma>();
+  else if (nks > 1) wait_vmcnt<kDma>();
   else wait_vmcnt<0>();
   __syncthreads();
   Frags f0, f1;
-  if (nks > 0) read_frags(0, f0);
+  if (live && nks > 0) read_frags(0, f0);
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;
@@ -289,57 +317,41 @@ w4a4_gemm_kernel(int64_t M, int64_t N, int64_t K, const uint16_t* __restrict__ A
     if (ks + 2 < nks) step(I2{}, ks + 2, f0, f1);
     if (ks + 3 < nks) step(I3{}, ks + 3, f1, f0);
   }
-
-  // the two K halves: waves 4-7 hand their sums to waves 0-3 through the (now free) ring
-  __syncthreads();
-  v4f* red = reinterpret_cast<v4f*>(smem);        // [4 quadrants][16 subtiles][64 lanes]
-  if (kw == 1) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) red[((wave & 3) * 16 + 4 * i + j) * 64 + lane] = acc[i][j];
-  }
-  __syncthreads();
-  if (kw == 1) return;
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const v4f o = red[((wave & 3) * 16 + 4 * i + j) * 64 + lane];
-      acc[i][j][0] += o[0];
-      acc[i][j][1] += o[1];
-      acc[i][j][2] += o[2];
-      acc[i][j][3] += o[3];
-    }
+  if (!live) return;
 
   // low-rank step: acc += T[m][0:32] · L_up[0:32][n]  (one bf16 MFMA K step of 32)
   if (rank == 32) {
-    v8bf tf[4], lf[4];
+    v8bf tf[8], lf[6];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int64_t m = m0 + wm * 64 + 16 * i + l16;
+    for (int i = 0; i < 8; ++i) {
+      int64_t m = m0 + wm * 128 + 16 * i + l16;
+      if (m >= M) m = M - 1;
       tf[i] = __builtin_bit_cast(v8bf, *reinterpret_cast<const uint4*>(T + m * 32 + 8 * q));
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t n = n0 + wn * 64 + 16 * j + l16;
+    for (int j = 0; j < 6; ++j) {
+      int64_t n = n0 + wn * 96 + 16 * j + l16;
+      if (n >= N) n = N - 1;
       uint16_t u[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) u[e] = Lu[(int64_t)(8 * q + e) * N + n];
       lf[j] = __builtin_bit_cast(v8bf, u);
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 8; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lf[j], tf[i], acc[i][j], 0, 0, 0);
+      for (int j = 0; j < 6; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lf[j], tf[i], acc[i][j], 0, 0, 0);
   }
 
+  // lane (l16, q) holds columns n0 + 96 wn + 16 j + 4 q + (0..3) of row m0 + 128 wm + 16 i + l16
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int64_t row = m0 + wm * 64 + 16 * i + l16;
+  for (int i = 0; i < 8; ++i) {
+    const int64_t row = m0 + wm * 128 + 16 * i + l16;
+    if (row >= M) continue;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t n = n0 + wn * 64 + 16 * j + 4 * q;
+    for (int j = 0; j < 6; ++j) {
+      const int64_t n = n0 + wn * 96 + 16 * j + 4 * q;
+      if (n >= N) continue;                         // N % 16 == 0: a lane's 4 columns are all in or all out
       float v[4] = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
       if (bias) {
 #pragma unroll
@@ -369,7 +381,7 @@ hipError_t launch_w4a4(int64_t M, int64_t N, int64_t K, const uint8_t* a, const 
                        const uint16_t* l_down, const uint16_t* l_up, int32_t rank,
                        const uint16_t* bias, uint16_t* d, int64_t ldd, void* ws, int num_cus, hipStream_t st) {
   if (M == 0 || N == 0) return hipSuccess;
-  if (M % BM != 0 || N % BN != 0 || K % 128 != 0 || K == 0) return hipErrorInvalidValue;
+  if (M % 128 != 0 || N % 128 != 0 || K % 128 != 0 || K == 0) return hipErrorInvalidValue;
   uint8_t* w = reinterpret_cast<uint8_t*>(ws);
   uint16_t* Ah = reinterpret_cast<uint16_t*>(w);
   uint16_t* Bh = reinterpret_cast<uint16_t*>(w + align256((size_t)M * K * 2));
@@ -384,8 +396,9 @@ hipError_t launch_w4a4(int64_t M, int64_t N, int64_t K, const uint8_t* a, const 
   if (rank > 0)
     hipLaunchKernelGGL(w4a4_lowrank_down_kernel, dim3((unsigned)((M + 15) / 16)), dim3(256), 0, st, x_bf16, M, K,
                        LdT, T);
-  const int64_t tiles = (M / BM) * (N / BN);
-  hipLaunchKernelGGL(w4a4_gemm_kernel, dim3((unsigned)tiles), dim3(64 * kWaves), 0, st, M, N, K, Ah, Bh,
+  const int64_t tiles = ((M + w4::BM - 1) / w4::BM) * ((N + w4::BN - 1) / w4::BN);
+  const int64_t grid = (tiles + 7) / 8 * 8;          // a multiple of the XCD count (tile order above)
+  hipLaunchKernelGGL(w4a4_gemm_kernel, dim3((unsigned)grid), dim3(64 * w4::kWaves), 0, st, M, N, K, Ah, Bh,
                      rank > 0 ? T : nullptr, l_up, (int)rank, bias, d, ldd);
   return hipGetLastError();
 }

@@ -514,6 +514,16 @@ def test_w4a4_small():
     tol_check(y, ref, what="w4a4 small")
 
 
+@pytest.mark.gpu
+@pytest.mark.parametrize("M,N,K", [(384, 640, 256), (640, 384, 128), (1152, 896, 256)])
+def test_w4a4_partial_tiles(M, N, K):
+    # 256 x 192 workgroup tiles: partial tiles in M and N, fewer than four tile rows in the
+    # last raster group, tile counts that are not a multiple of the XCD count
+    wl = synth.w4a4(seed=79 + M, M=M, N=N, K=K)
+    y, ref = _w4a4_run(wl)
+    tol_check(y, ref, what=f"w4a4 {M}x{N}x{K}")
+
+
 def test_w4a4_no_epilogue():
     """No low-rank branch and no bias: the plain W4A4 product."""
     wl = synth.w4a4(seed=78, M=128, N=256, K=384)
