@@ -520,6 +520,10 @@ gemm_fp8_contig_kernel(int G, int64_t M, int64_t N, int64_t K, const uint8_t* __
       // 64 wm + 16 i + l16.  a = SiLU(gate) * up in fp32; the row's maximum over the 128
       // columns: over the lane's 8 values, the 4 lanes q (shuffles) and the 4 column
       // waves (LDS); s = max / 448 and the e4m3 codes (the rule of the 1x128 quantizer).
+      // The codes are those of a · (1/s) with the hardware reciprocal, without the exact
+      // quotient of the standalone quantizer: this path's inputs are fp32 GEMM sums, not
+      // the oracle's fp64 ones, so it is held to the oracle within a tolerance anyway, and
+      // a few-ulp quotient only moves a code that sits on an e4m3 rounding midpoint.
       const int lane_e = opaque(lane);
       const int le16 = lane_e & 15, qe = lane_e >> 4;
       float amax[4];
@@ -531,7 +535,10 @@ gemm_fp8_contig_kernel(int G, int64_t M, int64_t N, int64_t K, const uint8_t* __
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const float gv = acc[i][jj][e];
-            const float a = div_by_ge1(gv, 1.0f + exp_neg(gv)) * acc[i][jj + 2][e];
+            // e^-g from the hardware base-2 exponential, the quotient by the hardware
+            // reciprocal (a few ulps each; 1 + e^-g = inf gives 0)
+            const float ex = __builtin_amdgcn_exp2f(gv * -1.44269504088896341f);
+            const float a = gv * __builtin_amdgcn_rcpf(1.0f + ex) * acc[i][jj + 2][e];
             acc[i][jj][e] = a;
             amax[i] = fmaxf(amax[i], fabsf(a));
           }
@@ -561,8 +568,7 @@ gemm_fp8_contig_kernel(int G, int64_t M, int64_t N, int64_t K, const uint8_t* __
           for (int jj = 0; jj < 2; ++jj) {
             const v4f& a = acc[i][jj];
             *reinterpret_cast<uint32_t*>(qrow + 16 * jj) =
-                e4m3_pack4(e4m3_quotient(a[0], sc, rc), e4m3_quotient(a[1], sc, rc), e4m3_quotient(a[2], sc, rc),
-                           e4m3_quotient(a[3], sc, rc));
+                e4m3_pack4(a[0] * rc, a[1] * rc, a[2] * rc, a[3] * rc);
           }
           if (wn == 0 && qe == 0) S[cur.nt * M + row] = sc;
         }
