@@ -719,8 +719,9 @@ gemm_fp8_dense_kernel(int64_t M, int64_t N, int64_t K, const uint8_t* __restrict
 
     // One K block from LDS stage ST: B fragments first, then the A fragments
     // streamed one row tile ahead; program order pinned group by group: MFMA t,
-    // then (at t % 4 == 0) the reads of A row tile t/4 + 1, then the promotion
-    // of MFMA t-2 (three result registers in rotation).
+    // then the reads of A row tile t/4 + 1 (its low half after MFMA 4i, its high
+    // half after MFMA 4i + 1: measured ~1.5% faster than both after 4i), then the
+    // promotion of MFMA t-2 (three result registers in rotation).
     const float* sbl_w = reinterpret_cast<const float*>(smem + kSBOff) + ((wn * 64) / 128) * kMaxKb;
     auto compute = [&](auto st_tag, int kb) {
       constexpr int ST = decltype(st_tag)::value;
@@ -743,6 +744,7 @@ gemm_fp8_dense_kernel(int64_t M, int64_t N, int64_t K, const uint8_t* __restrict
       for (int i = 0; i < 8; ++i) sab[i] = *reinterpret_cast<const float*>(sb + rs + i * 16 * 4) * sbv;
       __builtin_amdgcn_sched_barrier(0);
       v4f p[3];
+      uint4 alo;
 #pragma unroll
       for (int t = 0; t < 34; ++t) {
         if (t < 32) {
@@ -753,9 +755,12 @@ gemm_fp8_dense_kernel(int64_t M, int64_t N, int64_t K, const uint8_t* __restrict
         __builtin_amdgcn_sched_barrier(0);
         if (t < 28 && (t & 3) == 0) {
           const int i = (t >> 2) + 1;
-          const uint4 lo = *reinterpret_cast<const uint4*>(sb + ra_lo + i * 16 * BK);
+          alo = *reinterpret_cast<const uint4*>(sb + ra_lo + i * 16 * BK);
+        }
+        if (t < 29 && (t & 3) == 1) {
+          const int i = (t >> 2) + 1;
           const uint4 hi = *reinterpret_cast<const uint4*>(sb + ra_hi + i * 16 * BK);
-          af[i & 1] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+          af[i & 1] = v8i{(int)alo.x, (int)alo.y, (int)alo.z, (int)alo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
         }
         if (t >= 2) {
           const int u = t - 2;
