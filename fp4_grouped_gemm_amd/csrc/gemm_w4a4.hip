@@ -41,27 +41,6 @@ __device__ inline float e2m1_f32(uint32_t nib, float s) {
   return f * s;
 }
 
-// dequantize 32 packed E2M1 values (16 bytes, two 16-element groups) to fp16
-__device__ inline void dequant32(uint4 packed, float s0, float s1, uint4* out4) {
-  const uint32_t w[4] = {packed.x, packed.y, packed.z, packed.w};
-  uint32_t h[16];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float s = (i < 2) ? s0 : s1;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t byte = (w[i] >> (8 * j)) & 0xFFu;
-      const _Float16 lo = (_Float16)e2m1_f32(byte & 0xFu, s);
-      const _Float16 hi = (_Float16)e2m1_f32(byte >> 4, s);
-      h[4 * i + j] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
-    }
-  }
-  out4[0] = make_uint4(h[0], h[1], h[2], h[3]);
-  out4[1] = make_uint4(h[4], h[5], h[6], h[7]);
-  out4[2] = make_uint4(h[8], h[9], h[10], h[11]);
-  out4[3] = make_uint4(h[12], h[13], h[14], h[15]);
-}
-
 __device__ inline void dma16(const void* sbase, uint32_t voff, uint32_t lds) {
   uint32_t save;
   asm volatile(
@@ -82,19 +61,22 @@ __device__ inline void wait_vmcnt() {
 
 // The GEMM's operand preparation in one launch, by block ranges: packed E2M1 rows with
 // fp32 scales per 16 -> fp16 (x·s rounded once), for A ([M][K/2] -> [M][K]) and B,
-// one thread per 32 elements; then, with the low-rank branch, L_down [K][32] ->
+// one thread per 8 elements (4 code bytes in, 16 bytes out: consecutive lanes write
+// consecutive 16-byte pieces); then, with the low-rank branch, L_down [K][32] ->
 // LdT [32][K] (bf16), so that both operands of T = X·L_down are K-contiguous.
-__device__ inline void dequant_item(const uint8_t* __restrict__ q, const float* __restrict__ s, int64_t i,
-                                    uint16_t* __restrict__ out) {
-  const uint4 p = *reinterpret_cast<const uint4*>(q + i * 16);
-  const float2 sc = *reinterpret_cast<const float2*>(s + i * 2);
-  uint4 h[4];
-  dequant32(p, sc.x, sc.y, h);
-  uint4* o = reinterpret_cast<uint4*>(out + i * 32);
-  o[0] = h[0];
-  o[1] = h[1];
-  o[2] = h[2];
-  o[3] = h[3];
+__device__ inline void dequant_item8(const uint8_t* __restrict__ q, const float* __restrict__ s, int64_t i,
+                                     uint16_t* __restrict__ out) {
+  const uint32_t w = *reinterpret_cast<const uint32_t*>(q + i * 4);
+  const float sc = s[i >> 1];                     // elements 8i..8i+7 lie in 16-element group i/2
+  uint32_t h[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t byte = (w >> (8 * j)) & 0xFFu;
+    const _Float16 lo = (_Float16)e2m1_f32(byte & 0xFu, sc);
+    const _Float16 hi = (_Float16)e2m1_f32(byte >> 4, sc);
+    h[j] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+  }
+  *reinterpret_cast<uint4*>(out + i * 8) = make_uint4(h[0], h[1], h[2], h[3]);
 }
 
 __global__ void __launch_bounds__(256) w4a4_prep_kernel(const uint8_t* __restrict__ qa, const float* __restrict__ sa,
@@ -107,10 +89,10 @@ __global__ void __launch_bounds__(256) w4a4_prep_kernel(const uint8_t* __restric
   const int64_t blk = blockIdx.x;
   if (blk < ba) {
     const int64_t i = blk * 256 + threadIdx.x;
-    if (i < na) dequant_item(qa, sa, i, ah);
+    if (i < na) dequant_item8(qa, sa, i, ah);
   } else if (blk < ba + bb) {
     const int64_t i = (blk - ba) * 256 + threadIdx.x;
-    if (i < nb) dequant_item(qb, sb, i, bh);
+    if (i < nb) dequant_item8(qb, sb, i, bh);
   } else {
     const int64_t i = (blk - ba - bb) * 256 + threadIdx.x;   // over K*32, rank fastest (coalesced reads)
     if (i < nld) LdT[(i & 31) * K + (i >> 5)] = Ld[i];
@@ -118,20 +100,21 @@ __global__ void __launch_bounds__(256) w4a4_prep_kernel(const uint8_t* __restric
 }
 
 // T[m][r] = Σ_k X[m][k] · L_down[k][r] (rank 32), fp32 accumulate, stored bf16.
-// One 256-thread block per 16 rows; wave w sums K range [w·K/4, (w+1)·K/4) with
+// One block of NW waves per 16 rows; wave w sums K range [w·K/NW, (w+1)·K/NW) with
 // v_mfma_f32_16x16x32_bf16 (first operand: 16 ranks of LdT, second: the 16 X
 // rows; lane (l, q) holds K elements [8q, 8q+8) of row l of each), two rank
-// tiles per wave; the four partial sums are added in wave order through LDS.
-__global__ void __launch_bounds__(256) w4a4_lowrank_down_kernel(const uint16_t* __restrict__ X, int64_t M, int64_t K,
-                                                                 const uint16_t* __restrict__ LdT,
-                                                                 uint16_t* __restrict__ T) {
-  __shared__ v4f part[4][2][64];
+// tiles per wave; the partial sums are added in wave order through LDS.
+template <int NW>
+__global__ void __launch_bounds__(64 * NW) w4a4_lowrank_down_kernel(const uint16_t* __restrict__ X, int64_t M, int64_t K,
+                                                                     const uint16_t* __restrict__ LdT,
+                                                                     uint16_t* __restrict__ T) {
+  __shared__ v4f part[NW][2][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l16 = lane & 15, q = lane >> 4;
   const int64_t m0 = (int64_t)blockIdx.x * 16;
   int64_t mrow = m0 + l16;
   if (mrow >= M) mrow = M - 1;               // rows past the end read a valid row; never stored
-  const int64_t kq = K / 4;                  // K % 128 == 0, so kq % 32 == 0
+  const int64_t kq = K / NW;                 // a multiple of 32 (checked at launch)
   const int64_t k_begin = wave * kq, k_end = k_begin + kq;
   const uint16_t* xr = X + mrow * K + 8 * q;
   const uint16_t* l0 = LdT + (int64_t)l16 * K + 8 * q;
@@ -161,7 +144,7 @@ __global__ void __launch_bounds__(256) w4a4_lowrank_down_kernel(const uint16_t* 
   // lane (l16, q) holds ranks 4q..4q+3 (tile 0) and 16+4q.. (tile 1) of row m0 + l16
   v4f s0 = part[0][0][lane], s1 = part[0][1][lane];
 #pragma unroll
-  for (int w = 1; w < 4; ++w) {
+  for (int w = 1; w < NW; ++w) {
     const v4f a = part[w][0][lane], b = part[w][1][lane];
     s0[0] += a[0]; s0[1] += a[1]; s0[2] += a[2]; s0[3] += a[3];
     s1[0] += b[0]; s1[1] += b[1]; s1[2] += b[2]; s1[3] += b[3];
@@ -387,15 +370,21 @@ hipError_t launch_w4a4(int64_t M, int64_t N, int64_t K, const uint8_t* a, const 
   uint16_t* Bh = reinterpret_cast<uint16_t*>(w + align256((size_t)M * K * 2));
   uint8_t* rest = w + align256((size_t)M * K * 2) + align256((size_t)N * K * 2);
   (void)num_cus;
-  const int64_t na = M * K / 32, nb = N * K / 32, nld = rank > 0 ? K * 32 : 0;
+  const int64_t na = M * K / 8, nb = N * K / 8, nld = rank > 0 ? K * 32 : 0;
   uint16_t* T = reinterpret_cast<uint16_t*>(rest);
   uint16_t* LdT = reinterpret_cast<uint16_t*>(rest + align256((size_t)M * 32 * 2));
   const int64_t blocks = (na + 255) / 256 + (nb + 255) / 256 + (nld + 255) / 256;
   hipLaunchKernelGGL(w4a4_prep_kernel, dim3((unsigned)blocks), dim3(256), 0, st, a, sa, na, Ah, b, sb, nb, Bh,
                      l_down, nld, rank > 0 ? LdT : nullptr, K);
-  if (rank > 0)
-    hipLaunchKernelGGL(w4a4_lowrank_down_kernel, dim3((unsigned)((M + 15) / 16)), dim3(256), 0, st, x_bf16, M, K,
-                       LdT, T);
+  if (rank > 0) {
+    // eight waves per 16 rows when K/8 is a multiple of 32 (more waves in flight), else four
+    if (K % 256 == 0)
+      hipLaunchKernelGGL(w4a4_lowrank_down_kernel<8>, dim3((unsigned)((M + 15) / 16)), dim3(512), 0, st, x_bf16, M,
+                         K, LdT, T);
+    else
+      hipLaunchKernelGGL(w4a4_lowrank_down_kernel<4>, dim3((unsigned)((M + 15) / 16)), dim3(256), 0, st, x_bf16, M,
+                         K, LdT, T);
+  }
   const int64_t tiles = ((M + w4::BM - 1) / w4::BM) * ((N + w4::BN - 1) / w4::BN);
   const int64_t grid = (tiles + 7) / 8 * 8;          // a multiple of the XCD count (tile order above)
   hipLaunchKernelGGL(w4a4_gemm_kernel, dim3((unsigned)grid), dim3(64 * w4::kWaves), 0, st, M, N, K, Ah, Bh,
