@@ -16,8 +16,8 @@
 // first) and one extra bf16 MFMA step T·L_up per output tile, before the bias
 // is added in the epilogue.
 //
-// GEMM tile: 256 x 192 per 512-thread workgroup, two waves per SIMD, each wave 128 x 48
-// outputs (96 fp32 accumulators); a 4-buffer LDS ring of 32-wide K stages filled by
+// GEMM tile: 256 x 192 per 1024-thread workgroup, four waves per SIMD, each wave 64 x 48
+// outputs (48 fp32 accumulators); a 4-buffer LDS ring of 32-wide K stages filled by
 // global_load_lds_dwordx4 two stages ahead, the next stage's fragments read into
 // registers while the current stage's MFMAs run (details at the kernel).  Measured on
 // MI355X, v_mfma_f32_16x16x32_f16 issues at about 1.3 PFLOP/s when fed from registers
@@ -159,15 +159,16 @@ __global__ void __launch_bounds__(64 * NW) w4a4_lowrank_down_kernel(const uint16
 }
 
 // The fp16 GEMM D = A_h · B_hᵀ (+ T · L_up) (+ bias), bf16 out.  Workgroup tile 256 x 192,
-// eight waves (two per SIMD) of 128 x 48 outputs: 8 x 3 MFMA subtiles, 96 fp32
-// accumulators per lane.  With one wave per SIMD (four waves of 128 x 96, accumulators in
-// the accumulation registers, 299 instead of 469 bytes of LDS reads per MFMA) the call
-// took 11% longer: a lone wave's barrier waits and DMA issue leave its SIMD's matrix core
-// idle, a second wave fills them.  The 4096 x 3072 shape is exactly 256 tiles, one per CU.
+// sixteen waves (four per SIMD) of 64 x 48 outputs: 4 x 3 MFMA subtiles, 48 fp32
+// accumulators per lane, at most 128 VGPRs per wave.  Measured alternatives on the same
+// tile: one wave per SIMD (128 x 96 each, accumulators in the accumulation registers,
+// 299 bytes of LDS reads per MFMA) 16% slower for the whole call, two per SIMD (128 x 48)
+// 5% slower: a SIMD's other waves issue MFMAs while one waits at the barrier or issues
+// its DMA.  The 4096 x 3072 shape is exactly 256 tiles, one per CU.
 // K stages of 32 (one MFMA step): 256 A rows + 192 B rows of 64 bytes = 28 KB, a
 // 4-buffer ring filled by global_load_lds_dwordx4 (waves 0-3, 7 DMA instructions each
 // per stage) two stages ahead; the next stage's fragments are read while the current
-// stage's 24 MFMAs run.  A 64-byte row's four 16-byte chunks are XOR-swizzled with
+// stage's 12 MFMAs run.  A 64-byte row's four 16-byte chunks are XOR-swizzled with
 // (row >> 2) & 3, so the 16 lanes of one quarter-wave (16 rows, one chunk index) hit
 // 16 distinct bank groups.  Rows past M or N read the last valid row (never stored).
 namespace w4 {
@@ -176,17 +177,17 @@ constexpr int kRowBytes = BK * 2;                 // 64
 constexpr int kABytes = BM * kRowBytes;           // 16 KB
 constexpr int kStageBytes = (BM + BN) * kRowBytes;  // 28 KB
 constexpr int kStages = 4;
-constexpr int kWaves = 8;                         // two per SIMD: 2 row x 4 column waves
+constexpr int kWaves = 16;                        // four per SIMD: 4 row x 4 column waves
 constexpr int kDmaWaves = 4;                      // waves 0-3 issue the stage DMA
 constexpr int kDma = kStageBytes / 1024 / kDmaWaves; // 7
-constexpr int kWC = 48, kNJ = 3;                  // a wave's columns and column subtiles
+constexpr int kWC = 48, kNJ = 3;                  // a wave's columns and column subtiles (64 rows)
 constexpr int kAGroups = kABytes / 1024;          // 16 (16 rows per KB)
 constexpr int kGM = 4;                            // tile rows per raster group
 static_assert(kStages * kStageBytes <= 160 * 1024, "LDS budget");
 __device__ inline int key(int row) { return (row >> 2) & 3; }
 }  // namespace w4
 
-__global__ void __launch_bounds__(512, 1)
+__global__ void __launch_bounds__(1024, 1)
 w4a4_gemm_kernel(int64_t M, int64_t N, int64_t K, const uint16_t* __restrict__ Ah, const uint16_t* __restrict__ Bh,
                  const uint16_t* __restrict__ T, const uint16_t* __restrict__ Lu, int rank,
                  const uint16_t* __restrict__ bias, uint16_t* __restrict__ D, int64_t ldd) {
@@ -196,7 +197,7 @@ w4a4_gemm_kernel(int64_t M, int64_t N, int64_t K, const uint16_t* __restrict__ A
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave & 1, wn = wave >> 1;      // wn in 0..3
+  const int wm = wave & 3, wn = wave >> 2;      // 64 rows, 48 columns each
   const int l16 = lane & 15, q = lane >> 4;
 
   // Tile order: consecutive tile indices go to one XCD (workgroup b runs on XCD b % 8),
@@ -210,12 +211,12 @@ w4a4_gemm_kernel(int64_t M, int64_t N, int64_t K, const uint16_t* __restrict__ A
   const int64_t idx = t - group * kGM * nN;
   const int64_t m0 = (first_m + idx % gm) * BM, n0 = (idx / gm) * BN;
   const int rows = (int)((M - m0) < BM ? (M - m0) : BM), cols = (int)((N - n0) < BN ? (N - n0) : BN);
-  const bool live = (wm * 128 < rows) && (wn * kWC < cols);
+  const bool live = (wm * 64 < rows) && (wn * kWC < cols);
   const int nks = (int)(K / BK);
 
   // DMA roles: a stage is 28 segments of 1 KB (16 rows of 64 bytes), segments 0-15 the A
-  // rows, 16-27 the B rows; wave w < 4 issues segments 7w .. 7w+6 (waves 4-7 none, so
-  // their vmcnt waits return at once).  Lane l fills chunk l % 4
+  // rows, 16-27 the B rows; wave w < 4 issues segments 7w .. 7w+6 (the other waves none,
+  // so their vmcnt waits return at once).  Lane l fills chunk l % 4
   // of row l / 4 of its segment and reads source chunk (l % 4) ^ key(row).
   const uint8_t* Abase = reinterpret_cast<const uint8_t*>(Ah + m0 * K);
   const uint8_t* Bbase = reinterpret_cast<const uint8_t*>(Bh + n0 * K);
@@ -239,24 +240,24 @@ w4a4_gemm_kernel(int64_t M, int64_t N, int64_t K, const uint16_t* __restrict__ A
     }
   };
 
-  v4f acc[8][kNJ];
+  v4f acc[4][kNJ];
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < kNJ; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
   // fragments: lane (l16, q) takes 8 fp16 (K [8q, 8q+8) of the stage) of rows 16 i + l16
   // of the wave's A rows and of its B rows; rows 16 apart share a swizzle key
-  const int arow = wm * 128 + l16, brow = BM + wn * kWC + l16;
+  const int arow = wm * 64 + l16, brow = BM + wn * kWC + l16;
   const int a_off = arow * kRowBytes + ((q ^ key(arow)) << 4);
   const int b_off = brow * kRowBytes + ((q ^ key(brow)) << 4);
   struct Frags {
-    v8h a[8], b[kNJ];
+    v8h a[4], b[kNJ];
   };
   auto read_frags = [&](int slot, Frags& f) {
     const uint8_t* base = smem + slot * kStageBytes;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) f.a[i] = *reinterpret_cast<const v8h*>(base + a_off + 16 * i * kRowBytes);
+    for (int i = 0; i < 4; ++i) f.a[i] = *reinterpret_cast<const v8h*>(base + a_off + 16 * i * kRowBytes);
 #pragma unroll
     for (int j = 0; j < kNJ; ++j) f.b[j] = *reinterpret_cast<const v8h*>(base + b_off + 16 * j * kRowBytes);
   };
@@ -277,7 +278,7 @@ w4a4_gemm_kernel(int64_t M, int64_t N, int64_t K, const uint16_t* __restrict__ A
     if (live) {
       if (ks + 1 < nks) read_frags((ST + 1) % kStages, nxt);
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < kNJ; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(cur.b[j], cur.a[i], acc[i][j], 0, 0, 0);
@@ -308,10 +309,10 @@ w4a4_gemm_kernel(int64_t M, int64_t N, int64_t K, const uint16_t* __restrict__ A
 
   // low-rank step: acc += T[m][0:32] · L_up[0:32][n]  (one bf16 MFMA K step of 32)
   if (rank == 32) {
-    v8bf tf[8], lf[kNJ];
+    v8bf tf[4], lf[kNJ];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      int64_t m = m0 + wm * 128 + 16 * i + l16;
+    for (int i = 0; i < 4; ++i) {
+      int64_t m = m0 + wm * 64 + 16 * i + l16;
       if (m >= M) m = M - 1;
       tf[i] = __builtin_bit_cast(v8bf, *reinterpret_cast<const uint4*>(T + m * 32 + 8 * q));
     }
@@ -325,15 +326,15 @@ w4a4_gemm_kernel(int64_t M, int64_t N, int64_t K, const uint16_t* __restrict__ A
       lf[j] = __builtin_bit_cast(v8bf, u);
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < kNJ; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lf[j], tf[i], acc[i][j], 0, 0, 0);
   }
 
-  // lane (l16, q) holds columns n0 + 48 wn + 16 j + 4 q + (0..3) of row m0 + 128 wm + 16 i + l16
+  // lane (l16, q) holds columns n0 + 48 wn + 16 j + 4 q + (0..3) of row m0 + 64 wm + 16 i + l16
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int64_t row = m0 + wm * 128 + 16 * i + l16;
+  for (int i = 0; i < 4; ++i) {
+    const int64_t row = m0 + wm * 64 + 16 * i + l16;
     if (row >= M) continue;
 #pragma unroll
     for (int j = 0; j < kNJ; ++j) {
