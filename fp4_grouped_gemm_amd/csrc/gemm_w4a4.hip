@@ -17,11 +17,10 @@
 // is added in the epilogue.
 //
 // GEMM tile: 256 x 192 per 1024-thread workgroup, four waves per SIMD, each wave 64 x 48
-// outputs (48 fp32 accumulators); a 4-buffer LDS ring of 32-wide K stages filled by
-// global_load_lds_dwordx4 two stages ahead, the next stage's fragments read into
-// registers while the current stage's MFMAs run (details at the kernel).  Measured on
-// MI355X, v_mfma_f32_16x16x32_f16 issues at about 1.3 PFLOP/s when fed from registers
-// only (half the 2.5 PFLOP/s fp16 figure), which bounds this path.
+// outputs (48 fp32 accumulators); two LDS buffers of 64-wide K stages filled by
+// global_load_lds_dwordx4 one stage ahead (details at the kernel).  Measured on MI355X,
+// v_mfma_f32_16x16x32_f16 issues at about 1.3 PFLOP/s when fed from registers only (half
+// the 2.5 PFLOP/s fp16 figure), which bounds this path.
 #include <algorithm>
 #include <type_traits>
 
@@ -165,26 +164,29 @@ __global__ void __launch_bounds__(64 * NW) w4a4_lowrank_down_kernel(const uint16
 // 299 bytes of LDS reads per MFMA) 16% slower for the whole call, two per SIMD (128 x 48)
 // 5% slower: a SIMD's other waves issue MFMAs while one waits at the barrier or issues
 // its DMA.  The 4096 x 3072 shape is exactly 256 tiles, one per CU.
-// K stages of 32 (one MFMA step): 256 A rows + 192 B rows of 64 bytes = 28 KB, a
-// 4-buffer ring filled by global_load_lds_dwordx4 (waves 0-3, 7 DMA instructions each
-// per stage) two stages ahead; the next stage's fragments are read while the current
-// stage's 12 MFMAs run.  A 64-byte row's four 16-byte chunks are XOR-swizzled with
-// (row >> 2) & 3, so the 16 lanes of one quarter-wave (16 rows, one chunk index) hit
-// 16 distinct bank groups.  Rows past M or N read the last valid row (never stored).
+// K stages of 64 (two MFMA steps): 256 A rows + 192 B rows of 128 bytes = 56 KB, two
+// buffers, the DMA of stage ks + 1 (waves 0-7, 7 instructions each) issued right after the
+// barrier of step ks; a step reads both halves' fragments at its top and runs 24 MFMAs
+// (the SIMD's other waves cover the read latency).  Measured against a 4-buffer ring of
+// 32-wide stages two ahead with the next stage's fragments read during the current
+// MFMAs: 4% faster for the whole call (half the barriers).  A 128-byte row's eight
+// 16-byte chunks are XOR-swizzled with (row & 7) ^ ((row >> 3) & 1), so the 16 rows of
+// one fragment read hit distinct bank groups.  Rows past M or N read the last valid row
+// (never stored).
 namespace w4 {
-constexpr int BM = 256, BN = 192, BK = 32;
-constexpr int kRowBytes = BK * 2;                 // 64
-constexpr int kABytes = BM * kRowBytes;           // 16 KB
-constexpr int kStageBytes = (BM + BN) * kRowBytes;  // 28 KB
-constexpr int kStages = 4;
+constexpr int BM = 256, BN = 192, BK = 64;
+constexpr int kRowBytes = BK * 2;                 // 128
+constexpr int kABytes = BM * kRowBytes;           // 32 KB
+constexpr int kStageBytes = (BM + BN) * kRowBytes;  // 56 KB
+constexpr int kStages = 2;
 constexpr int kWaves = 16;                        // four per SIMD: 4 row x 4 column waves
-constexpr int kDmaWaves = 4;                      // waves 0-3 issue the stage DMA
+constexpr int kDmaWaves = 8;                      // waves 0-7 issue the stage DMA
 constexpr int kDma = kStageBytes / 1024 / kDmaWaves; // 7
 constexpr int kWC = 48, kNJ = 3;                  // a wave's columns and column subtiles (64 rows)
-constexpr int kAGroups = kABytes / 1024;          // 16 (16 rows per KB)
+constexpr int kAGroups = kABytes / 1024;          // 32 (8 rows per KB)
 constexpr int kGM = 4;                            // tile rows per raster group
 static_assert(kStages * kStageBytes <= 160 * 1024, "LDS budget");
-__device__ inline int key(int row) { return (row >> 2) & 3; }
+__device__ inline int key(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 }  // namespace w4
 
 __global__ void __launch_bounds__(1024, 1)
@@ -214,21 +216,21 @@ w4a4_gemm_kernel(int64_t M, int64_t N, int64_t K, const uint16_t* __restrict__ A
   const bool live = (wm * 64 < rows) && (wn * kWC < cols);
   const int nks = (int)(K / BK);
 
-  // DMA roles: a stage is 28 segments of 1 KB (16 rows of 64 bytes), segments 0-15 the A
-  // rows, 16-27 the B rows; wave w < 4 issues segments 7w .. 7w+6 (the other waves none,
-  // so their vmcnt waits return at once).  Lane l fills chunk l % 4
-  // of row l / 4 of its segment and reads source chunk (l % 4) ^ key(row).
+  // DMA roles: a stage is 56 segments of 1 KB (8 rows of 128 bytes), segments 0-31 the A
+  // rows, 32-55 the B rows; wave w < 8 issues segments 7w .. 7w+6 (the other waves none,
+  // so their vmcnt waits return at once).  Lane l fills chunk l % 8 of row l / 8 of its
+  // segment and reads source chunk (l % 8) ^ key(row).
   const uint8_t* Abase = reinterpret_cast<const uint8_t*>(Ah + m0 * K);
   const uint8_t* Bbase = reinterpret_cast<const uint8_t*>(Bh + n0 * K);
   uint32_t voff[kDma];
 #pragma unroll
   for (int i = 0; i < kDma; ++i) {
     const int seg = wave * kDma + i;
-    const int row = seg * 16 + (lane >> 2);          // row of the stage ([A rows][B rows])
+    const int row = seg * 8 + (lane >> 3);           // row of the stage ([A rows][B rows])
     int src = seg < kAGroups ? row : row - BM;
     const int lim = seg < kAGroups ? rows : cols;
     if (src >= lim) src = lim - 1;
-    voff[i] = (uint32_t)src * (uint32_t)(K * 2) + (uint32_t)((((lane & 3) ^ key(row))) * 16);
+    voff[i] = (uint32_t)src * (uint32_t)(K * 2) + (uint32_t)((((lane & 7) ^ key(row))) * 16);
   }
   auto issue = [&](int ks, int stage) {
     if (wave >= kDmaWaves) return;
@@ -246,64 +248,45 @@ w4a4_gemm_kernel(int64_t M, int64_t N, int64_t K, const uint16_t* __restrict__ A
 #pragma unroll
     for (int j = 0; j < kNJ; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  // fragments: lane (l16, q) takes 8 fp16 (K [8q, 8q+8) of the stage) of rows 16 i + l16
-  // of the wave's A rows and of its B rows; rows 16 apart share a swizzle key
+  // fragments: lane (l16, q) takes 8 fp16 (K [32h + 8q, 32h + 8q + 8) of half h of the
+  // stage) of rows 16 i + l16 of the wave's A rows and of its B rows; rows 16 apart share
+  // a swizzle key
   const int arow = wm * 64 + l16, brow = BM + wn * kWC + l16;
-  const int a_off = arow * kRowBytes + ((q ^ key(arow)) << 4);
-  const int b_off = brow * kRowBytes + ((q ^ key(brow)) << 4);
   struct Frags {
     v8h a[4], b[kNJ];
   };
-  auto read_frags = [&](int slot, Frags& f) {
+  auto read_frags = [&](int slot, int h, Frags& f) {
     const uint8_t* base = smem + slot * kStageBytes;
+    const int ao = arow * kRowBytes + (((4 * h + q) ^ key(arow)) << 4);
+    const int bo = brow * kRowBytes + (((4 * h + q) ^ key(brow)) << 4);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) f.a[i] = *reinterpret_cast<const v8h*>(base + a_off + 16 * i * kRowBytes);
+    for (int i = 0; i < 4; ++i) f.a[i] = *reinterpret_cast<const v8h*>(base + ao + 16 * i * kRowBytes);
 #pragma unroll
-    for (int j = 0; j < kNJ; ++j) f.b[j] = *reinterpret_cast<const v8h*>(base + b_off + 16 * j * kRowBytes);
+    for (int j = 0; j < kNJ; ++j) f.b[j] = *reinterpret_cast<const v8h*>(base + bo + 16 * j * kRowBytes);
   };
-  // top of step ks: this wave's reads of stage ks done and its DMA of stage ks + 1 landed
-  // (stage ks + 2 may fly); the barrier makes both true for every wave, so stage ks + 1
-  // is readable and the buffer of stage ks - 1 is free for stage ks + 3.
-  auto step = [&](auto st_tag, int ks, const Frags& cur, Frags& nxt) {
-    constexpr int ST = decltype(st_tag)::value;     // == ks % kStages
-    __builtin_amdgcn_s_waitcnt(0xC07F);             // lgkmcnt(0)
-    // stages issued after stage ks + 1 (up to ks + kStages - 2) may still fly
-    const int last = (ks + kStages - 2) < (nks - 1) ? (ks + kStages - 2) : (nks - 1);
-    const int after = last - (ks + 1);
-    if (after >= 2) wait_vmcnt<2 * kDma>();
-    else if (after == 1) wait_vmcnt<kDma>();
-    else wait_vmcnt<0>();
-    __syncthreads();
-    if (ks + kStages - 1 < nks) issue(ks + kStages - 1, (ST + kStages - 1) % kStages);
-    if (live) {
-      if (ks + 1 < nks) read_frags((ST + 1) % kStages, nxt);
+  auto mma = [&](const Frags& f) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < kNJ; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(cur.b[j], cur.a[i], acc[i][j], 0, 0, 0);
-    }
+      for (int j = 0; j < kNJ; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(f.b[j], f.a[i], acc[i][j], 0, 0, 0);
   };
-  static_assert(kStages == 4, "the prologue and the unrolled loop below assume a 4-buffer ring");
+  // top of step ks: this wave's DMA of stage ks landed and its reads of the other buffer
+  // (step ks - 1) done; the barrier makes both true for every wave, so stage ks is
+  // readable and the other buffer takes stage ks + 1.  Both halves' fragments are read
+  // at the top (the other waves of the SIMD cover the latency).
   if (nks > 0) issue(0, 0);
-  if (nks > 1) issue(1, 1);
-  if (nks > 2) issue(2, 2);
-  // stage 0 landed (two stages may fly)
-  if (nks > 2) wait_vmcnt<2 * kDma>();
-  else if (nks > 1) wait_vmcnt<kDma>();
-  else wait_vmcnt<0>();
-  __syncthreads();
-  Frags f0, f1;
-  if (live && nks > 0) read_frags(0, f0);
-  using I0 = std::integral_constant<int, 0>;
-  using I1 = std::integral_constant<int, 1>;
-  using I2 = std::integral_constant<int, 2>;
-  using I3 = std::integral_constant<int, 3>;
-  for (int ks = 0; ks < nks; ks += 4) {
-    step(I0{}, ks, f0, f1);
-    if (ks + 1 < nks) step(I1{}, ks + 1, f1, f0);
-    if (ks + 2 < nks) step(I2{}, ks + 2, f0, f1);
-    if (ks + 3 < nks) step(I3{}, ks + 3, f1, f0);
+  for (int ks = 0; ks < nks; ++ks) {
+    wait_vmcnt<0>();
+    __syncthreads();
+    if (ks + 1 < nks) issue(ks + 1, (ks + 1) & 1);
+    if (live) {
+      Frags f0, f1;
+      read_frags(ks & 1, 0, f0);
+      read_frags(ks & 1, 1, f1);
+      mma(f0);
+      mma(f1);
+    }
   }
   if (!live) return;
 
