@@ -62,22 +62,20 @@ __host__ __device__ inline uint32_t e2m1_encode(float v) {
 }
 
 // fl32(x / s) as far as the e4m3 code of it is concerned, given r = rcp(s).
-// One Newton step after the reciprocal product leaves q within one ulp of the
-// correctly rounded quotient.  That neighbourhood can change the e4m3 code only
-// when q sits within a few ulps of a rounding midpoint (the 20 bits below the
-// 3 kept mantissa bits near 0x80000), below the normal e4m3 range (a finer
-// grid), or far above 448 / not finite (degenerate scales); those lanes take
-// the IEEE division, every other lane's code equals that of the exact quotient.
-// Requires s > 0.
+// The hardware reciprocal is within one ulp, so q = x·r lies within about 3.5 ulps of
+// the correctly rounded quotient.  That neighbourhood can change the e4m3 code only
+// when q sits near a rounding midpoint (the 20 bits below the 3 kept mantissa bits
+// near 0x80000: lanes within 8 ulps of it), below the normal e4m3 range (a finer grid),
+// or far above 448 / not finite (degenerate scales); those lanes take the IEEE
+// division, every other lane's code equals that of the exact quotient (checked on
+// 2^30 uniform and 2^30 midpoint-adjacent (x, s) pairs on MI355X: no difference).
+// q = x·r keeps x's sign, also for zero.  Requires s > 0.
 __device__ inline float e4m3_quotient(float x, float s, float r) {
   float q = x * r;
-  const float e = __builtin_fmaf(-q, s, x);
-  q = __builtin_fmaf(e, r, q);
   const uint32_t a = __float_as_uint(q) & 0x7FFFFFFFu;
-  const bool risky = (a - 1u < 0x3C7FFFFFu) | ((a & 0xFFFFFu) - 0x7FFFDu < 7u) | (a > 0x43E80000u);
+  const bool risky = (a < 0x3C800000u) | ((a & 0xFFFFFu) - 0x7FFF8u < 16u) | (a > 0x43E80000u);
   if (__builtin_expect(risky, 0)) q = x / s;
-  // s > 0, so the quotient carries x's sign; the correction step turns -0 into +0
-  return __builtin_copysignf(q, x);
+  return q;
 }
 
 // Four e4m3 codes packed little-endian (v0 in the low byte), by the gfx950
