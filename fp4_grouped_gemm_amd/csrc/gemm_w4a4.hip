@@ -60,22 +60,39 @@ __device__ inline void wait_vmcnt() {
 
 // The GEMM's operand preparation in one launch, by block ranges: packed E2M1 rows with
 // fp32 scales per 16 -> fp16 (x·s rounded once), for A ([M][K/2] -> [M][K]) and B,
-// one thread per 8 elements (4 code bytes in, 16 bytes out: consecutive lanes write
-// consecutive 16-byte pieces); then, with the low-rank branch, L_down [K][32] ->
-// LdT [32][K] (bf16), so that both operands of T = X·L_down are K-contiguous.
-__device__ inline void dequant_item8(const uint8_t* __restrict__ q, const float* __restrict__ s, int64_t i,
-                                     uint16_t* __restrict__ out) {
-  const uint32_t w = *reinterpret_cast<const uint32_t*>(q + i * 4);
-  const float sc = s[i >> 1];                     // elements 8i..8i+7 lie in 16-element group i/2
-  uint32_t h[4];
+// 8 elements per item (4 code bytes in, 16 bytes out), kItems items per thread at a
+// stride of 256 so that each store instruction writes consecutive 16-byte pieces and
+// every load of a thread is in flight before its first conversion; then, with the
+// low-rank branch, L_down [K][32] -> LdT [32][K] (bf16), so that both operands of
+// T = X·L_down are K-contiguous.
+constexpr int kItems = 4;
+
+__device__ inline void dequant_items(const uint8_t* __restrict__ q, const float* __restrict__ s, int64_t base,
+                                     int64_t n, uint16_t* __restrict__ out) {
+  uint32_t w[kItems];
+  float sc[kItems];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const uint32_t byte = (w >> (8 * j)) & 0xFFu;
-    const _Float16 lo = (_Float16)e2m1_f32(byte & 0xFu, sc);
-    const _Float16 hi = (_Float16)e2m1_f32(byte >> 4, sc);
-    h[j] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+  for (int j = 0; j < kItems; ++j) {
+    const int64_t i = base + 256 * j;
+    if (i < n) {
+      w[j] = *reinterpret_cast<const uint32_t*>(q + i * 4);
+      sc[j] = s[i >> 1];                          // elements 8i..8i+7 lie in 16-element group i/2
+    }
   }
-  *reinterpret_cast<uint4*>(out + i * 8) = make_uint4(h[0], h[1], h[2], h[3]);
+#pragma unroll
+  for (int j = 0; j < kItems; ++j) {
+    const int64_t i = base + 256 * j;
+    if (i >= n) break;
+    uint32_t h[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const uint32_t byte = (w[j] >> (8 * b)) & 0xFFu;
+      const _Float16 lo = (_Float16)e2m1_f32(byte & 0xFu, sc[j]);
+      const _Float16 hi = (_Float16)e2m1_f32(byte >> 4, sc[j]);
+      h[b] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+    }
+    *reinterpret_cast<uint4*>(out + i * 8) = make_uint4(h[0], h[1], h[2], h[3]);
+  }
 }
 
 __global__ void __launch_bounds__(256) w4a4_prep_kernel(const uint8_t* __restrict__ qa, const float* __restrict__ sa,
@@ -84,14 +101,13 @@ __global__ void __launch_bounds__(256) w4a4_prep_kernel(const uint8_t* __restric
                                                         int64_t nb, uint16_t* __restrict__ bh,
                                                         const uint16_t* __restrict__ Ld, int64_t nld,
                                                         uint16_t* __restrict__ LdT, int64_t K) {
-  const int64_t ba = (na + 255) / 256, bb = (nb + 255) / 256;
+  constexpr int64_t kPer = 256 * kItems;
+  const int64_t ba = (na + kPer - 1) / kPer, bb = (nb + kPer - 1) / kPer;
   const int64_t blk = blockIdx.x;
   if (blk < ba) {
-    const int64_t i = blk * 256 + threadIdx.x;
-    if (i < na) dequant_item8(qa, sa, i, ah);
+    dequant_items(qa, sa, blk * kPer + threadIdx.x, na, ah);
   } else if (blk < ba + bb) {
-    const int64_t i = (blk - ba) * 256 + threadIdx.x;
-    if (i < nb) dequant_item8(qb, sb, i, bh);
+    dequant_items(qb, sb, (blk - ba) * kPer + threadIdx.x, nb, bh);
   } else {
     const int64_t i = (blk - ba - bb) * 256 + threadIdx.x;   // over K*32, rank fastest (coalesced reads)
     if (i < nld) LdT[(i & 31) * K + (i >> 5)] = Ld[i];
@@ -361,7 +377,8 @@ hipError_t launch_w4a4(int64_t M, int64_t N, int64_t K, const uint8_t* a, const 
   const int64_t na = M * K / 8, nb = N * K / 8, nld = rank > 0 ? K * 32 : 0;
   uint16_t* T = reinterpret_cast<uint16_t*>(rest);
   uint16_t* LdT = reinterpret_cast<uint16_t*>(rest + align256((size_t)M * 32 * 2));
-  const int64_t blocks = (na + 255) / 256 + (nb + 255) / 256 + (nld + 255) / 256;
+  const int64_t per = 256 * kItems;
+  const int64_t blocks = (na + per - 1) / per + (nb + per - 1) / per + (nld + 255) / 256;
   hipLaunchKernelGGL(w4a4_prep_kernel, dim3((unsigned)blocks), dim3(256), 0, st, a, sa, na, Ah, b, sb, nb, Bh,
                      l_down, nld, rank > 0 ? LdT : nullptr, K);
   if (rank > 0) {
