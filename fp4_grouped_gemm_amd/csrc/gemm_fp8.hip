@@ -396,10 +396,11 @@ gemm_fp8_contig_kernel(int G, int64_t M, int64_t N, int64_t K, const uint8_t* __
       v8i b[kNFrag];
       float s[4];
     };
-    auto load_frags = [&](auto st_tag, Frags& f) {
+    auto load_frags = [&](auto st_tag, auto ni_tag, Frags& f) {
       constexpr int ST = decltype(st_tag)::value;
+      constexpr int NI = decltype(ni_tag)::value;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < NI; ++i) {
         const uint4 lo = *reinterpret_cast<const uint4*>(smem + ra_lo + ST * kABytes + i * 16 * BK);
         const uint4 hi = *reinterpret_cast<const uint4*>(smem + ra_hi + ST * kABytes + i * 16 * BK);
         f.a[i] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
@@ -420,19 +421,23 @@ gemm_fp8_contig_kernel(int G, int64_t M, int64_t N, int64_t K, const uint8_t* __
     // The promotion therefore trails its MFMA by two MFMA issues (three result
     // registers in rotation), so the matrix core never waits for the vector ALU
     // and no FMA waits for a result still in flight.
-    auto mma_and_read = [&](const Frags& f, const float (&sb)[2], auto nst_tag, Frags& nxt) {
+    // NI: the wave's row fragments (16 rows each) that hold valid rows; the MFMAs, reads
+    // and promotions of the others are left out (a partial last tile of a segment).
+    auto mma_and_read = [&](const Frags& f, const float (&sb)[2], auto nst_tag, auto ni_tag, Frags& nxt) {
       constexpr int NST = decltype(nst_tag)::value;
+      constexpr int NI = decltype(ni_tag)::value;
       constexpr int NH = SILU ? 2 : 1;              // weight-scale blocks per wave
       float sab[NH][4];
 #pragma unroll
       for (int h = 0; h < NH; ++h)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sab[h][i] = f.s[i] * sb[h];
+        for (int i = 0; i < NI; ++i) sab[h][i] = f.s[i] * sb[h];
       constexpr int T = 4 * kNFrag;
       v4f p[3];
       uint4 rd[20];
       auto read = [&](int r) {
         // reads 0..7: A fragments (lo, hi); 8..11: activation scales; 12..19: B fragments
+        if ((r < 8 && (r >> 1) >= NI) || (r >= 8 && r < 12 && r - 8 >= NI)) return;
         if (r < 8) {
           const int i = r >> 1;
           const uint32_t off = ((r & 1) ? ra_hi : ra_lo) + NST * kABytes + i * 16 * BK;
@@ -448,7 +453,7 @@ gemm_fp8_contig_kernel(int G, int64_t M, int64_t N, int64_t K, const uint8_t* __
       };
 #pragma unroll
       for (int t = 0; t < T + 2; ++t) {
-        if (t < T) {
+        if (t < T && t / kNFrag < NI) {
           p[t % 3] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
               f.b[t % kNFrag], f.a[t / kNFrag], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
         }
@@ -459,7 +464,7 @@ gemm_fp8_contig_kernel(int G, int64_t M, int64_t N, int64_t K, const uint8_t* __
         } else if (t < 14) {
           read(t + 6);
         }
-        if (t >= 2) {
+        if (t >= 2 && (t - 2) / kNFrag < NI) {
           const int u = t - 2;
           const v4f& r = p[u % 3];
           v4f& c = acc[u / kNFrag][u % kNFrag];
@@ -472,7 +477,7 @@ gemm_fp8_contig_kernel(int G, int64_t M, int64_t N, int64_t K, const uint8_t* __
         __builtin_amdgcn_sched_barrier(0);
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < NI; ++i) {
         const uint4 lo = rd[2 * i], hi = rd[2 * i + 1];
         nxt.a[i] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
       }
@@ -494,8 +499,9 @@ gemm_fp8_contig_kernel(int G, int64_t M, int64_t N, int64_t K, const uint8_t* __
       sb_cur[0] = sbl_w[slot * (kSBStage / 4)];
       if constexpr (SILU) sb_cur[1] = sbl_w[slot * (kSBStage / 4) + 1];
     };
-    auto step = [&](auto st_tag, Frags& cf, Frags& nf, int kb) {
+    auto step = [&](auto st_tag, auto ni_tag, Frags& cf, Frags& nf, int kb) {
       constexpr int ST = decltype(st_tag)::value;       // == kb % 3
+      constexpr int NI = decltype(ni_tag)::value;
       // all of this wave's LDS reads (the fragments of stage kb, the scale) are done:
       // a real s_waitcnt the compiler sees, so it needs no wait inside the MFMA run
       __builtin_amdgcn_s_waitcnt(kLgkmZero);
@@ -509,7 +515,7 @@ gemm_fp8_contig_kernel(int G, int64_t M, int64_t N, int64_t K, const uint8_t* __
       if (kb + 3 < nkb) issue(kb + 3, ST);
       // unconditional for busy waves (the last step's reads are unused but in bounds):
       // the reads and the MFMAs stay in one basic block, interleaved in a fixed order
-      if (busy) mma_and_read(cf, sb_cur, std::integral_constant<int, (ST + 1) % kStages>{}, nf);
+      if constexpr (NI > 0) mma_and_read(cf, sb_cur, std::integral_constant<int, (ST + 1) % kStages>{}, ni_tag, nf);
       // stage kb + 1's weight scale (complete since this step's barrier), waited at the
       // next step's top; after the last step the slot is stale and unused
       read_sb((ST + 1) % kStages);
@@ -520,20 +526,31 @@ gemm_fp8_contig_kernel(int G, int64_t M, int64_t N, int64_t K, const uint8_t* __
     wait_vmcnt<0>();
     __builtin_amdgcn_s_waitcnt(kLgkmZero);
     block_barrier();
-    Frags f0, f1;
-    if (busy) load_frags(std::integral_constant<int, 0>{}, f0);
-    read_sb(0);
-
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
     using I2 = std::integral_constant<int, 2>;
-    for (int kb = 0; kb < nkb; kb += 6) {
-      step(I0{}, f0, f1, kb);
-      if (kb + 1 < nkb) step(I1{}, f1, f0, kb + 1);
-      if (kb + 2 < nkb) step(I2{}, f0, f1, kb + 2);
-      if (kb + 3 < nkb) step(I0{}, f1, f0, kb + 3);
-      if (kb + 4 < nkb) step(I1{}, f0, f1, kb + 4);
-      if (kb + 5 < nkb) step(I2{}, f1, f0, kb + 5);
+    auto k_loop = [&](auto ni_tag) {
+      Frags f0, f1;
+      if constexpr (decltype(ni_tag)::value > 0) load_frags(I0{}, ni_tag, f0);
+      read_sb(0);
+      for (int kb = 0; kb < nkb; kb += 6) {
+        step(I0{}, ni_tag, f0, f1, kb);
+        if (kb + 1 < nkb) step(I1{}, ni_tag, f1, f0, kb + 1);
+        if (kb + 2 < nkb) step(I2{}, ni_tag, f0, f1, kb + 2);
+        if (kb + 3 < nkb) step(I0{}, ni_tag, f1, f0, kb + 3);
+        if (kb + 4 < nkb) step(I1{}, ni_tag, f0, f1, kb + 4);
+        if (kb + 5 < nkb) step(I2{}, ni_tag, f1, f0, kb + 5);
+      }
+    };
+    // row fragments of this wave with valid rows (wave-uniform)
+    const int nvalid = cur.rows_valid - wm * 64;
+    const int ni = nvalid <= 0 ? 0 : nvalid >= 64 ? 4 : (nvalid + 15) >> 4;
+    switch (ni) {
+      case 4: k_loop(std::integral_constant<int, 4>{}); break;
+      case 3: k_loop(std::integral_constant<int, 3>{}); break;
+      case 2: k_loop(std::integral_constant<int, 2>{}); break;
+      case 1: k_loop(std::integral_constant<int, 1>{}); break;
+      default: k_loop(std::integral_constant<int, 0>{}); break;
     }
 
     // The next tile's first stages.  With SILU they are fetched now, behind the long
