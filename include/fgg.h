@@ -199,7 +199,7 @@ fgg_status fgg_moe_permute_quantize(const int32_t* topk_ids, int64_t T, int32_t 
  *   computed); when given, masked_m[g] (clamped to [0, segment length]) is
  *   group g's number of real rows, e.g. the permute's counts, and the rows
  *   [offsets[g] + masked_m[g], offsets[g+1]) are padding: not written, and
- *   their MFMA work is skipped in 64-row units (their A rows may still be
+ *   their MFMA work is skipped in 16-row units (their A rows may still be
  *   read).  aq = {E4M3,F32,1,128}: a [M][K], a_scales [K/128][M];
  *   bq = {E4M3,F32,128,128}: b [G][N][K], b_scales [G][N/128][K/128].
  * FGG_LAYOUT_MASKED (decode, K >= 128): A is [G][M][K] (M = rows per group, <= 16);
