@@ -118,6 +118,9 @@ def test_grouped_contiguous_small(counts, N, K):
     assert np.all(np.isnan(y[mt:]))                            # rows >= offsets[G] untouched
 
 
+_FRAG_COUNTS = [1, 15, 16, 17, 32, 33, 48, 63, 64, 65, 80, 81, 96, 112, 113, 127, 128, 129]
+
+
 def _valid_rows(offsets, masked):
     """Rows [offsets[e], offsets[e] + clamp(masked[e], 0, segment length)) per group."""
     rows = []
@@ -131,7 +134,10 @@ def _valid_rows(offsets, masked):
     ([5, 0, 300, 128], [5, 0, 300, 128], 256, 512),        # tiles with 5 and 44 real rows
     ([5, 0, 300, 128], [2000, 7, -3, 64], 256, 512),       # clamped above / below, half tile
     ([129, 1000], [129, 1000], 384, 1024),
-    ([64, 65], [64, 65], 128, 256)])                       # exactly one busy row half, and one more row
+    ([64, 65], [64, 65], 128, 256),                        # exactly one busy row half, and one more row
+    # every 16-row fragment boundary of both row halves of a tile (a wave computes only
+    # the fragments that hold real rows)
+    (_FRAG_COUNTS, _FRAG_COUNTS, 256, 384)])
 def test_grouped_contiguous_valid_counts(counts, masked, N, K):
     """Per-group real row counts (masked_m with the contiguous layout): the rows
     they cover equal the unmasked call bit for bit; padding rows past them are
@@ -610,7 +616,8 @@ def test_grouped_silu_quantize_small(counts, I, K):
 
 
 @pytest.mark.parametrize("counts,masked,I,K", [([5, 0, 300, 128], [5, 0, 300, 128], 128, 512),
-                                               ([5, 0, 300, 128], [2000, 7, -3, 64], 256, 512)])
+                                               ([5, 0, 300, 128], [2000, 7, -3, 64], 256, 512),
+                                               (_FRAG_COUNTS, _FRAG_COUNTS, 128, 384)])
 def test_grouped_silu_quantize_valid_counts(counts, masked, I, K):
     """Per-group real row counts: the rows they cover equal the call without
     counts bit for bit; codes and scales of padding rows are not written."""
