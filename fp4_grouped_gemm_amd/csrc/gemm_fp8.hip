@@ -46,8 +46,8 @@
 //    share are fetched once into that XCD's L2; a tile's expert is found by
 //    binary search over the workgroup's LDS copy of the segment offsets
 //    (segments are multiples of 128 rows, so a tile never straddles two
-//    experts), and with per-expert row counts, tiles and 64-row halves that hold
-//    only padding are skipped.
+//    experts), and with per-expert row counts, tiles that hold only padding are
+//    skipped and a wave computes only its 16-row fragments that hold real rows.
 #include <type_traits>
 
 #include "fgg_device.hpp"
@@ -380,7 +380,8 @@ gemm_fp8_contig_kernel(int G, int64_t M, int64_t N, int64_t K, const uint8_t* __
   while (true) {
     Tile nxt;
     const bool have_next = find_tile(cur.st + kXcds, nxt);
-    // a wave whose 64 rows are all padding only helps move data
+    // a wave whose 64 rows are all padding only helps move data (and the K loop below
+    // runs the instance for the wave's number of fragments with real rows)
     const bool busy = wm * 64 < cur.rows_valid;
 
     v4f acc[4][kNFrag];
