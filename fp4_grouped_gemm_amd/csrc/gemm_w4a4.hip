@@ -11,10 +11,10 @@
 // element exactly once; dequantizing inside the GEMM made each workgroup redo
 // the tiles it shares with N/128 or M/128 others and left the kernel bound by
 // that vector-ALU work), and contracted with v_mfma_f32_16x16x32_f16 in fp32.
-// The low-rank branch is a separate small bf16-MFMA kernel for T = X·L_down
-// (fp32 accumulate, stored bf16 in the workspace, with L_down transposed there
-// first) and one extra bf16 MFMA step T·L_up per output tile, before the bias
-// is added in the epilogue.
+// The low-rank branch is T = X·L_down on bf16 MFMA (fp32 accumulate, stored bf16
+// in the workspace), computed by its own blocks of the operand-preparation launch,
+// and one extra bf16 MFMA step T·L_up per output tile, before the bias is added in
+// the epilogue.
 //
 // GEMM tile: 256 x 192 per 1024-thread workgroup, four waves per SIMD, each wave 64 x 48
 // outputs (48 fp32 accumulators); two LDS buffers of 64-wide K stages filled by
@@ -58,14 +58,24 @@ __device__ inline void wait_vmcnt() {
 }
 }  // namespace
 
-// The GEMM's operand preparation in one launch, by block ranges: packed E2M1 rows with
-// fp32 scales per 16 -> fp16 (x·s rounded once), for A ([M][K/2] -> [M][K]) and B,
-// 8 elements per item (4 code bytes in, 16 bytes out), kItems items per thread at a
-// stride of 256 so that each store instruction writes consecutive 16-byte pieces and
-// every load of a thread is in flight before its first conversion; then, with the
-// low-rank branch, L_down [K][32] -> LdT [32][K] (bf16), so that both operands of
-// T = X·L_down are K-contiguous.
+// The GEMM's operand preparation and the low-rank branch in one launch, by block
+// ranges, so that the two run side by side:
+//  * blocks [0, M/16) (with the low-rank branch): T[m][r] = Σ_k X[m][k] · L_down[k][r]
+//    (rank 32) for 16 rows each, fp32 accumulate, stored bf16.  Wave w sums K range
+//    [w·K/4, (w+1)·K/4) with v_mfma_f32_16x16x32_bf16 (first operand: 16 ranks of
+//    L_down, second: the 16 X rows; lane (l, q) holds K elements [8q, 8q+8) of row l of
+//    each), two rank tiles per wave.  L_down is [K][32] (ranks contiguous): a wave
+//    loads each 32-row slice of it and writes it transposed into its own LDS area
+//    ([32 ranks][32 k]), from which the rank-major fragments are read (a wave's LDS
+//    operations take effect in program order).  The partial sums are added in wave
+//    order through LDS.
+//  * the following blocks: packed E2M1 rows with fp32 scales per 16 -> fp16 (x·s
+//    rounded once), for A ([M][K/2] -> [M][K]) and B, 8 elements per item (4 code
+//    bytes in, 16 bytes out), kItems items per thread at a stride of 256 so that each
+//    store instruction writes consecutive 16-byte pieces and every load of a thread is
+//    in flight before its first conversion.
 constexpr int kItems = 4;
+constexpr int kLrWaves = 4;
 
 __device__ inline void dequant_items(const uint8_t* __restrict__ q, const float* __restrict__ s, int64_t base,
                                      int64_t n, uint16_t* __restrict__ out) {
@@ -99,58 +109,53 @@ __global__ void __launch_bounds__(256) w4a4_prep_kernel(const uint8_t* __restric
                                                         int64_t na, uint16_t* __restrict__ ah,
                                                         const uint8_t* __restrict__ qb, const float* __restrict__ sb,
                                                         int64_t nb, uint16_t* __restrict__ bh,
-                                                        const uint16_t* __restrict__ Ld, int64_t nld,
-                                                        uint16_t* __restrict__ LdT, int64_t K) {
+                                                        const uint16_t* __restrict__ X, const uint16_t* __restrict__ Ld,
+                                                        uint16_t* __restrict__ T, int64_t M, int64_t K,
+                                                        int64_t lr_blocks) {
+  __shared__ __align__(16) uint16_t ldt[kLrWaves][32 * 32];
+  __shared__ v4f part[kLrWaves][2][64];
   constexpr int64_t kPer = 256 * kItems;
-  const int64_t ba = (na + kPer - 1) / kPer, bb = (nb + kPer - 1) / kPer;
   const int64_t blk = blockIdx.x;
-  if (blk < ba) {
-    dequant_items(qa, sa, blk * kPer + threadIdx.x, na, ah);
-  } else if (blk < ba + bb) {
-    dequant_items(qb, sb, (blk - ba) * kPer + threadIdx.x, nb, bh);
-  } else {
-    const int64_t i = (blk - ba - bb) * 256 + threadIdx.x;   // over K*32, rank fastest (coalesced reads)
-    if (i < nld) LdT[(i & 31) * K + (i >> 5)] = Ld[i];
+  if (blk >= lr_blocks) {
+    const int64_t ba = (na + kPer - 1) / kPer;
+    const int64_t pb = blk - lr_blocks;
+    if (pb < ba) dequant_items(qa, sa, pb * kPer + threadIdx.x, na, ah);
+    else dequant_items(qb, sb, (pb - ba) * kPer + threadIdx.x, nb, bh);
+    return;
   }
-}
-
-// T[m][r] = Σ_k X[m][k] · L_down[k][r] (rank 32), fp32 accumulate, stored bf16.
-// One block of NW waves per 16 rows; wave w sums K range [w·K/NW, (w+1)·K/NW) with
-// v_mfma_f32_16x16x32_bf16 (first operand: 16 ranks of LdT, second: the 16 X
-// rows; lane (l, q) holds K elements [8q, 8q+8) of row l of each), two rank
-// tiles per wave; the partial sums are added in wave order through LDS.
-template <int NW>
-__global__ void __launch_bounds__(64 * NW) w4a4_lowrank_down_kernel(const uint16_t* __restrict__ X, int64_t M, int64_t K,
-                                                                     const uint16_t* __restrict__ LdT,
-                                                                     uint16_t* __restrict__ T) {
-  __shared__ v4f part[NW][2][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l16 = lane & 15, q = lane >> 4;
-  const int64_t m0 = (int64_t)blockIdx.x * 16;
+  const int64_t m0 = blk * 16;
   int64_t mrow = m0 + l16;
   if (mrow >= M) mrow = M - 1;               // rows past the end read a valid row; never stored
-  const int64_t kq = K / NW;                 // a multiple of 32 (checked at launch)
+  const int64_t kq = K / kLrWaves;           // a multiple of 32 (K % 128 == 0)
   const int64_t k_begin = wave * kq, k_end = k_begin + kq;
   const uint16_t* xr = X + mrow * K + 8 * q;
-  const uint16_t* l0 = LdT + (int64_t)l16 * K + 8 * q;
-  const uint16_t* l1 = LdT + (int64_t)(16 + l16) * K + 8 * q;
+  uint16_t* tl = ldt[wave];
+  const int kk = lane >> 1, rb = 16 * (lane & 1);   // the L_down elements this lane moves
+  const bool ld_vec = (reinterpret_cast<uintptr_t>(Ld) & 15u) == 0;
   v4f acc0 = v4f{0.f, 0.f, 0.f, 0.f}, acc1 = v4f{0.f, 0.f, 0.f, 0.f};
-  for (int64_t k = k_begin; k < k_end; k += 128) {
-    uint4 xa[4], la[4], lb[4];
+  for (int64_t k = k_begin; k < k_end; k += 32) {
+    const uint16_t* src = Ld + (k + kk) * 32 + rb;  // row k + kk, ranks rb .. rb + 15
+    const uint4 xa = *reinterpret_cast<const uint4*>(xr + k);
+    if (ld_vec) {
+      const uint4 r0 = *reinterpret_cast<const uint4*>(src);
+      const uint4 r1 = *reinterpret_cast<const uint4*>(src + 8);
+      const uint32_t w[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      if (k + 32 * u >= k_end) break;       // wave-uniform: the range is a multiple of 32
-      xa[u] = *reinterpret_cast<const uint4*>(xr + k + 32 * u);
-      la[u] = *reinterpret_cast<const uint4*>(l0 + k + 32 * u);
-      lb[u] = *reinterpret_cast<const uint4*>(l1 + k + 32 * u);
-    }
+      for (int e = 0; e < 8; ++e) {
+        tl[(rb + 2 * e) * 32 + kk] = (uint16_t)(w[e] & 0xFFFFu);
+        tl[(rb + 2 * e + 1) * 32 + kk] = (uint16_t)(w[e] >> 16);
+      }
+    } else {                                          // L_down only 2-byte aligned
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      if (k + 32 * u >= k_end) break;
-      const v8bf xv = __builtin_bit_cast(v8bf, xa[u]);
-      acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, la[u]), xv, acc0, 0, 0, 0);
-      acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, lb[u]), xv, acc1, 0, 0, 0);
+      for (int e = 0; e < 16; ++e) tl[(rb + e) * 32 + kk] = src[e];
     }
+    const uint4 la = *reinterpret_cast<const uint4*>(tl + l16 * 32 + 8 * q);
+    const uint4 lb = *reinterpret_cast<const uint4*>(tl + (16 + l16) * 32 + 8 * q);
+    const v8bf xv = __builtin_bit_cast(v8bf, xa);
+    acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, la), xv, acc0, 0, 0, 0);
+    acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, lb), xv, acc1, 0, 0, 0);
   }
   part[wave][0][lane] = acc0;
   part[wave][1][lane] = acc1;
@@ -159,7 +164,7 @@ __global__ void __launch_bounds__(64 * NW) w4a4_lowrank_down_kernel(const uint16
   // lane (l16, q) holds ranks 4q..4q+3 (tile 0) and 16+4q.. (tile 1) of row m0 + l16
   v4f s0 = part[0][0][lane], s1 = part[0][1][lane];
 #pragma unroll
-  for (int w = 1; w < NW; ++w) {
+  for (int w = 1; w < kLrWaves; ++w) {
     const v4f a = part[w][0][lane], b = part[w][1][lane];
     s0[0] += a[0]; s0[1] += a[1]; s0[2] += a[2]; s0[3] += a[3];
     s1[0] += b[0]; s1[1] += b[1]; s1[2] += b[2]; s1[3] += b[3];
@@ -352,14 +357,14 @@ w4a4_gemm_kernel(int64_t M, int64_t N, int64_t K, const uint16_t* __restrict__ A
 }
 
 // workspace: A and B dequantized to fp16 ([M][K], [N][K]), then with the low-rank
-// branch T [M][32] bf16 and LdT [32][K] bf16; every part 256-byte aligned
+// branch T [M][32] bf16; every part 256-byte aligned
 namespace {
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 }  // namespace
 
 size_t w4a4_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t rank) {
   size_t b = align256((size_t)M * K * 2) + align256((size_t)N * K * 2);
-  if (rank > 0) b += align256((size_t)M * 32 * 2) + align256((size_t)32 * K * 2);
+  if (rank > 0) b += align256((size_t)M * 32 * 2);
   return b;
 }
 
@@ -374,22 +379,13 @@ hipError_t launch_w4a4(int64_t M, int64_t N, int64_t K, const uint8_t* a, const 
   uint16_t* Bh = reinterpret_cast<uint16_t*>(w + align256((size_t)M * K * 2));
   uint8_t* rest = w + align256((size_t)M * K * 2) + align256((size_t)N * K * 2);
   (void)num_cus;
-  const int64_t na = M * K / 8, nb = N * K / 8, nld = rank > 0 ? K * 32 : 0;
+  const int64_t na = M * K / 8, nb = N * K / 8;
   uint16_t* T = reinterpret_cast<uint16_t*>(rest);
-  uint16_t* LdT = reinterpret_cast<uint16_t*>(rest + align256((size_t)M * 32 * 2));
   const int64_t per = 256 * kItems;
-  const int64_t blocks = (na + per - 1) / per + (nb + per - 1) / per + (nld + 255) / 256;
+  const int64_t lr_blocks = rank > 0 ? (M + 15) / 16 : 0;
+  const int64_t blocks = lr_blocks + (na + per - 1) / per + (nb + per - 1) / per;
   hipLaunchKernelGGL(w4a4_prep_kernel, dim3((unsigned)blocks), dim3(256), 0, st, a, sa, na, Ah, b, sb, nb, Bh,
-                     l_down, nld, rank > 0 ? LdT : nullptr, K);
-  if (rank > 0) {
-    // eight waves per 16 rows when K/8 is a multiple of 32 (more waves in flight), else four
-    if (K % 256 == 0)
-      hipLaunchKernelGGL(w4a4_lowrank_down_kernel<8>, dim3((unsigned)((M + 15) / 16)), dim3(512), 0, st, x_bf16, M,
-                         K, LdT, T);
-    else
-      hipLaunchKernelGGL(w4a4_lowrank_down_kernel<4>, dim3((unsigned)((M + 15) / 16)), dim3(256), 0, st, x_bf16, M,
-                         K, LdT, T);
-  }
+                     x_bf16, l_down, rank > 0 ? T : nullptr, M, K, lr_blocks);
   const int64_t tiles = ((M + w4::BM - 1) / w4::BM) * ((N + w4::BN - 1) / w4::BN);
   const int64_t grid = (tiles + 7) / 8 * 8;          // a multiple of the XCD count (tile order above)
   hipLaunchKernelGGL(w4a4_gemm_kernel, dim3((unsigned)grid), dim3(64 * w4::kWaves), 0, st, M, N, K, Ah, Bh,

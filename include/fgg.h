@@ -292,7 +292,7 @@ fgg_status fgg_pack_fp4_weights(const void* b, const void* b_scales, int32_t G, 
  *   Requires M % 128 == 0, K % 128 == 0, 128 <= K <= 2^22, N % 128 == 0, rank in {0, 32}.
  *   workspace (256-byte aligned) must hold fgg_scaled_gemm_workspace() bytes:
  *   the fp16 copies of A and B, and with a low-rank branch the [M][32]
- *   intermediate and a [32][K] transposed copy of l_down.  The FP8 case needs none.
+ *   intermediate.  The FP8 case needs none.
  */
 fgg_status fgg_scaled_gemm_workspace(int64_t M, int64_t N, int64_t K, fgg_qdesc aq, fgg_qdesc bq,
                                      const fgg_epilogue* epi, size_t* bytes);
