@@ -17,7 +17,7 @@ __all__ = [
     "Q_E4M3_1x128", "Q_E4M3_128x128", "Q_E2M1_1x16", "Q_E2M1_E8M0_1x32", "Q_E2M1_E8M0_1x32_TILED",
     "quantize_blockwise", "moe_permute", "moe_permute_outputs", "moe_permute_workspace_bytes",
     "grouped_gemm_scaled", "grouped_gemm_silu_quantize", "pack_fp4_weights",
-    "scaled_gemm", "moe_combine", "set_num_cus",
+    "scaled_gemm", "moe_combine", "set_num_cus", "kernel_table", "kernel_compiled_lds",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -40,6 +40,13 @@ class FggError(RuntimeError):
 class QDesc(ctypes.Structure):
     _fields_ = [("data", ctypes.c_int32), ("scale", ctypes.c_int32),
                 ("block_rows", ctypes.c_int32), ("block_k", ctypes.c_int32)]
+
+
+class KernelInfo(ctypes.Structure):
+    _fields_ = [("kernel", ctypes.c_char_p), ("entry", ctypes.c_char_p), ("tile_m", ctypes.c_int32),
+                ("tile_n", ctypes.c_int32), ("tile_k", ctypes.c_int32), ("threads", ctypes.c_int32),
+                ("stages", ctypes.c_int32), ("stage_bytes", ctypes.c_int32), ("other_bytes", ctypes.c_int32),
+                ("lds_bytes", ctypes.c_int32)]
 
 
 class Epilogue(ctypes.Structure):
@@ -73,6 +80,9 @@ def load_library():
         "fgg_status_string": ([I32], ctypes.c_char_p),
         "fgg_last_hip_error": ([], I32),
         "fgg_set_num_cus": ([ctypes.c_int], I32),
+        "fgg_kernel_count": ([], I32),
+        "fgg_kernel_info_get": ([I32, ctypes.POINTER(KernelInfo)], I32),
+        "fgg_kernel_compiled_lds": ([I32, ctypes.POINTER(I64)], I32),
         "fgg_quantize_blockwise": ([P, I32, I64, I64, I64, I32, QDesc, P, P, P, P], I32),
         "fgg_moe_permute_workspace": ([I64, I32, I32, ctypes.POINTER(SZ)], I32),
         "fgg_moe_permute": ([P, I64, I32, I32, I32, P, P, I64, P, P, P, P, P, P, I64, P, SZ, P], I32),
@@ -113,6 +123,27 @@ def _q(desc):
 
 def set_num_cus(n: int) -> None:
     _check("fgg_set_num_cus", load_library().fgg_set_num_cus(int(n)))
+
+
+def kernel_table():
+    """Every kernel of the library with its tile and LDS budget (fgg_kernel_info_get)."""
+    lib = load_library()
+    out = []
+    for i in range(lib.fgg_kernel_count()):
+        ki = KernelInfo()
+        _check("fgg_kernel_info_get", lib.fgg_kernel_info_get(i, ctypes.byref(ki)))
+        d = {f: getattr(ki, f) for f, _ in KernelInfo._fields_}
+        d["kernel"] = d["kernel"].decode()
+        d["entry"] = d["entry"].decode()
+        out.append(d)
+    return out
+
+
+def kernel_compiled_lds(i: int) -> int:
+    """Static LDS bytes of kernel i as compiled (asks the HIP runtime; needs the GPU)."""
+    n = ctypes.c_int64(0)
+    _check("fgg_kernel_compiled_lds", load_library().fgg_kernel_compiled_lds(int(i), ctypes.byref(n)))
+    return n.value
 
 
 # ------------------------------------------------------------------ quantize

@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
@@ -24,14 +25,6 @@ struct DeviceInfo {
   int num_cus = 0;
 };
 DeviceInfo g_dev[kMaxDevices];
-
-bool debug_enabled() {
-  static const bool on = [] {
-    const char* e = std::getenv("FGG_DEBUG");
-    return e != nullptr && e[0] != '\0' && e[0] != '0';
-  }();
-  return on;
-}
 
 fgg_status hip_fail(hipError_t e) {
   g_last_hip_error = (int)e;
@@ -66,6 +59,43 @@ bool same_q(const fgg_qdesc& q, fgg_dtype data, fgg_dtype scale, int br, int bk)
 fgg_status finish(hipError_t e) { return e == hipSuccess ? FGG_OK : hip_fail(e); }
 
 }  // namespace
+
+namespace fgg {
+
+bool debug_enabled() {
+  static const bool on = [] {
+    const char* e = std::getenv("FGG_DEBUG");
+    return e != nullptr && e[0] != '\0' && e[0] != '0';
+  }();
+  return on;
+}
+
+void trace_launch(const KernelInfo& k, dim3 grid, const char* fmt, ...) {
+  if (!debug_enabled()) return;
+  char what[256];
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(what, sizeof what, fmt, ap);
+  va_end(ap);
+  std::fprintf(stderr, "[fgg] %s: %s | grid=%u threads=%d tile=%dx%dx%d lds=%d B (%d x %d stage + %d) \n", k.name,
+               what, grid.x * grid.y * grid.z, k.threads, k.tile_m, k.tile_n, k.tile_k, k.lds_bytes, k.stages,
+               k.stage_bytes, k.other_bytes);
+}
+
+int kernel_table(const KernelInfo* const** out) {
+  static const KernelInfo* const table[] = {
+      &kInfoQuantE4m3_1x128, &kInfoQuantE4m3_128x128, &kInfoQuantE2m1_1x16, &kInfoQuantE2m1E8m0_1x32,
+      &kInfoPermuteHist,     &kInfoPermuteScan,       &kInfoPermuteScatter, &kInfoPermuteGather,
+      &kInfoPermuteQuantize, &kInfoFill,              &kInfoCombine,        &kInfoFp8Contig,
+      &kInfoFp8ContigSilu,   &kInfoFp8Dense,          &kInfoMaskedFp4Tiled, &kInfoMaskedFp4,
+      &kInfoMaskedFp8,       &kInfoPackFp4,           &kInfoPackFp4Scales,  &kInfoW4a4Prep,
+      &kInfoW4a4Gemm,
+  };
+  *out = table;
+  return (int)(sizeof table / sizeof table[0]);
+}
+
+}  // namespace fgg
 
 extern "C" {
 
@@ -191,9 +221,6 @@ fgg_status fgg_grouped_gemm_scaled(fgg_layout layout, int32_t G, int64_t M, int6
     if (!offsets) return FGG_ERR_INVALID_VALUE;
     fgg_status st = device_check(&num_cus);
     if (st != FGG_OK) return st;
-    if (debug_enabled())
-      std::fprintf(stderr, "[fgg] grouped_gemm contiguous G=%d M=%lld N=%lld K=%lld tile=128x256 (grouped) grid=%d\n",
-                   G, (long long)M, (long long)N, (long long)K, num_cus);
     if (M == 0 || N == 0) return FGG_OK;
     return finish(fgg::launch_gemm_fp8_contig(G, M, N, K, (const uint8_t*)a, (const float*)a_scales,
                                               (const uint8_t*)b, (const float*)b_scales, offsets, masked_m,
@@ -328,6 +355,42 @@ fgg_status fgg_moe_combine(const void* y, int64_t ldy, const int32_t* src_to_row
   if (st != FGG_OK) return st;
   return finish(fgg::launch_combine((const uint16_t*)y, ldy, src_to_row, topk_w, T, k, N, (uint16_t*)out, ldo,
                                     (hipStream_t)stream));
+}
+
+int32_t fgg_kernel_count(void) {
+  const fgg::KernelInfo* const* t = nullptr;
+  return (int32_t)fgg::kernel_table(&t);
+}
+
+fgg_status fgg_kernel_info_get(int32_t i, fgg_kernel_info* info) {
+  const fgg::KernelInfo* const* t = nullptr;
+  const int n = fgg::kernel_table(&t);
+  if (i < 0 || i >= n || !info) return FGG_ERR_INVALID_VALUE;
+  const fgg::KernelInfo& k = *t[i];
+  info->kernel = k.name;
+  info->entry = k.entry;
+  info->tile_m = k.tile_m;
+  info->tile_n = k.tile_n;
+  info->tile_k = k.tile_k;
+  info->threads = k.threads;
+  info->stages = k.stages;
+  info->stage_bytes = k.stage_bytes;
+  info->other_bytes = k.other_bytes;
+  info->lds_bytes = k.lds_bytes;
+  return FGG_OK;
+}
+
+fgg_status fgg_kernel_compiled_lds(int32_t i, int64_t* bytes) {
+  const fgg::KernelInfo* const* t = nullptr;
+  const int n = fgg::kernel_table(&t);
+  if (i < 0 || i >= n || !bytes) return FGG_ERR_INVALID_VALUE;
+  fgg_status st = device_check(nullptr);
+  if (st != FGG_OK) return st;
+  hipFuncAttributes attr;
+  const hipError_t e = hipFuncGetAttributes(&attr, t[i]->fn);
+  if (e != hipSuccess) return hip_fail(e);
+  *bytes = (int64_t)attr.sharedSizeBytes;
+  return FGG_OK;
 }
 
 }  // extern "C"

@@ -8,6 +8,37 @@
 
 namespace fgg {
 
+// Static description of one kernel instance: its workgroup tile, threads and LDS
+// budget.  [W4A4] §6 traces a silent slowdown to a shared-memory budget that was
+// counted wrong (one buffer left out), and asks for every stage/buffer choice to be
+// tabulated and checked; lds_bytes = stages * stage_bytes + other_bytes is the
+// kernel's declared static LDS, which a test compares with the compiled kernel's.
+struct KernelInfo {
+  const char* name;      // kernel instance
+  const char* entry;     // C entry point(s) that launch it
+  int tile_m, tile_n, tile_k;   // workgroup tile (0: not a tiled kernel)
+  int threads;           // threads per workgroup
+  int stages;            // LDS ring stages (0: no ring)
+  int stage_bytes;       // LDS bytes per stage
+  int other_bytes;       // LDS outside the ring: group tables, scale caches, reductions
+  int lds_bytes;         // declared static LDS
+  const void* fn;        // the kernel (for hipFuncGetAttributes)
+};
+
+// Every kernel of the library, in a fixed order.
+int kernel_table(const KernelInfo* const** out);
+
+// FGG_DEBUG (environment, read once): one line per kernel launch on stderr with the
+// kernel, the problem, grid, threads, tile, LDS bytes and stages.
+bool debug_enabled();
+void trace_launch(const KernelInfo& k, dim3 grid, const char* fmt, ...) __attribute__((format(printf, 3, 4)));
+
+extern const KernelInfo kInfoQuantE4m3_1x128, kInfoQuantE4m3_128x128, kInfoQuantE2m1_1x16,
+    kInfoQuantE2m1E8m0_1x32, kInfoPermuteHist, kInfoPermuteScan, kInfoPermuteScatter, kInfoPermuteGather,
+    kInfoPermuteQuantize, kInfoFill, kInfoCombine, kInfoFp8Contig, kInfoFp8ContigSilu, kInfoFp8Dense,
+    kInfoMaskedFp4Tiled, kInfoMaskedFp4, kInfoMaskedFp8, kInfoPackFp4, kInfoPackFp4Scales, kInfoW4a4Prep,
+    kInfoW4a4Gemm;
+
 enum class QuantKind { E4M3_1x128, E4M3_128x128, E2M1_1x16, E2M1_E8M0_1x32 };
 
 hipError_t launch_quantize(const void* x, bool bf16, int64_t rows, int64_t cols, int64_t ldx,

@@ -189,7 +189,10 @@ gemm_fp8_contig_kernel(int G, int64_t M, int64_t N, int64_t K, const uint8_t* __
   const int wm = wave >> 2, wn = wave & 3;
   const int l16 = lane & 15, q = lane >> 4;
 
-  const int64_t m_end = offsets ? (int64_t)offsets[G] : M;
+  // rows past M are never read or written, also when offsets[G] exceeds M (a permute whose
+  // M_cap was too small still publishes the full M_total)
+  int64_t m_end = offsets ? (int64_t)offsets[G] : M;
+  if (m_end > M) m_end = M;
   const int64_t m_tiles = (m_end + BM - 1) / BM;
   // N % 128 == 0: a last tile may be half wide; with SILU, N = 2I and tile j covers
   // gate block j and up block j (I / 128 tiles)
@@ -868,6 +871,18 @@ gemm_fp8_dense_kernel(int64_t M, int64_t N, int64_t K, const uint8_t* __restrict
   }
 }
 
+const KernelInfo kInfoFp8Contig = {
+    "gemm_fp8_contig_kernel<plain>", "fgg_grouped_gemm_scaled (contiguous), fgg_scaled_gemm (fp8, >128 K blocks)",
+    BM, BN, BK, kThreads, kStages, kABytes + kSBytes + kBBytes + kSBStage, (2 * kMaxG + 1) * 4 + 2 * 4 * 64 * 4,
+    kLdsBytes, (const void*)gemm_fp8_contig_kernel<false>};
+const KernelInfo kInfoFp8ContigSilu = {
+    "gemm_fp8_contig_kernel<silu>", "fgg_grouped_gemm_silu_quantize", BM, BN, BK, kThreads, kStages,
+    kABytes + kSBytes + kBBytes + kSBStage, (2 * kMaxG + 1) * 4 + 2 * 4 * 64 * 4, kLdsBytes,
+    (const void*)gemm_fp8_contig_kernel<true>};
+const KernelInfo kInfoFp8Dense = {"gemm_fp8_dense_kernel", "fgg_scaled_gemm (fp8)", dense::BM, dense::BN, dense::BK,
+                                  dense::kThreads, 2, dense::kStageBytes, 2 * dense::kMaxKb * 4, dense::kLdsBytes,
+                                  (const void*)gemm_fp8_dense_kernel};
+
 hipError_t launch_gemm_fp8_contig(int32_t G, int64_t M, int64_t N, int64_t K, const uint8_t* a,
                                   const float* sa, const uint8_t* b, const float* sb,
                                   const int32_t* offsets, const int32_t* valid, uint16_t* d, int64_t ldd,
@@ -879,6 +894,8 @@ hipError_t launch_gemm_fp8_contig(int32_t G, int64_t M, int64_t N, int64_t K, co
     int64_t grid = (int64_t)num_cus;
     grid = (grid / kXcds) * kXcds;
     if (grid < kXcds * dense::kSM) grid = kXcds * dense::kSM;
+    trace_launch(kInfoFp8Dense, dim3((unsigned)grid), "M=%lld N=%lld K=%lld persistent", (long long)M, (long long)N,
+                 (long long)K);
     hipLaunchKernelGGL(gemm_fp8_dense_kernel, dim3((unsigned)grid), dim3(dense::kThreads), 0, st, M, N, K, a, sa,
                        b, sb, d, ldd);
     return hipGetLastError();
@@ -888,6 +905,8 @@ hipError_t launch_gemm_fp8_contig(int32_t G, int64_t M, int64_t N, int64_t K, co
   int64_t grid = (int64_t)num_cus;
   grid = (grid / kXcds) * kXcds;
   if (grid < kXcds * kSM) grid = kXcds * kSM;
+  trace_launch(kInfoFp8Contig, dim3((unsigned)grid), "G=%d M=%lld N=%lld K=%lld%s persistent", (int)G, (long long)M,
+               (long long)N, (long long)K, valid ? " counts" : "");
   hipLaunchKernelGGL(gemm_fp8_contig_kernel<false>, dim3((unsigned)grid), dim3(kThreads), 0, st, G, M, N, K, a,
                      sa, b, sb, offsets, valid, d, ldd, nullptr, nullptr);
   return hipGetLastError();
@@ -902,6 +921,8 @@ hipError_t launch_gemm_fp8_silu_quantize(int32_t G, int64_t M, int64_t I, int64_
   int64_t grid = (int64_t)num_cus;
   grid = (grid / kXcds) * kXcds;
   if (grid < kXcds * kSM) grid = kXcds * kSM;
+  trace_launch(kInfoFp8ContigSilu, dim3((unsigned)grid), "G=%d M=%lld I=%lld K=%lld%s persistent", (int)G,
+               (long long)M, (long long)I, (long long)K, valid ? " counts" : "");
   hipLaunchKernelGGL(gemm_fp8_contig_kernel<true>, dim3((unsigned)grid), dim3(kThreads), 0, st, G, M, 2 * I, K, a,
                      sa, b, sb, offsets, valid, nullptr, (int64_t)0, q, s);
   return hipGetLastError();

@@ -364,11 +364,23 @@ gemm_masked_fp4_lds_kernel(int G, int64_t M, int64_t N, int64_t K, const uint8_t
   *reinterpret_cast<uint2*>(drow) = make_uint2(lo, hi);
 }
 
+const KernelInfo kInfoMaskedFp4Tiled = {
+    "gemm_masked_fp4_lds_kernel<tiled>", "fgg_grouped_gemm_scaled (masked, E2M1X2_TILED + E8M0/32)", 16, 128, 512,
+    512, 2, MaskedLds<4>::kBufBytes, 0, MaskedLds<4>::kBytes, (const void*)gemm_masked_fp4_lds_kernel<4, 4, 8, true>};
+const KernelInfo kInfoMaskedFp4 = {
+    "gemm_masked_fp4_lds_kernel<plain>", "fgg_grouped_gemm_scaled (masked, E2M1X2 + E8M0/32)", 16, 128, 512, 512, 2,
+    MaskedLds<4>::kBufBytes, 0, MaskedLds<4>::kBytes, (const void*)gemm_masked_fp4_lds_kernel<4, 4, 8, false>};
+const KernelInfo kInfoMaskedFp8 = {"gemm_masked_v2_kernel<e4m3>", "fgg_grouped_gemm_scaled (masked, e4m3 128x128)",
+                                   16, 128, 512, 256, 0, 0, 0, 0,
+                                   (const void*)gemm_masked_v2_kernel<false, 2, 4, true>};
+
 hipError_t launch_gemm_masked(bool b_fp4, bool tiled, int32_t G, int64_t M, int64_t N, int64_t K,
                               const uint8_t* a, const float* sa, const uint8_t* b, const void* sb,
                               const int32_t* masked_m, uint16_t* d, int64_t ldd, hipStream_t st) {
   if (N % 128 != 0 || M > 16 || (tiled && !b_fp4)) return hipErrorInvalidValue;
   const dim3 grid((unsigned)((int64_t)G * (N / 128)));
+  trace_launch(b_fp4 ? (tiled ? kInfoMaskedFp4Tiled : kInfoMaskedFp4) : kInfoMaskedFp8, grid,
+               "G=%d M=%lld N=%lld K=%lld", (int)G, (long long)M, (long long)N, (long long)K);
   if (b_fp4 && tiled) {
     // 8 waves x 16 weight rows per workgroup, 4 K blocks per step and per activation chunk
     hipLaunchKernelGGL((gemm_masked_fp4_lds_kernel<4, 4, 8, true>), grid, dim3(512), 0, st, G, M, N, K, a, sa, b,
@@ -425,6 +437,11 @@ pack_fp4_scale_tiles_kernel(const uint8_t* __restrict__ s, uint8_t* __restrict__
   }
 }
 
+const KernelInfo kInfoPackFp4 = {"pack_fp4_tiles_kernel", "fgg_pack_fp4_weights", 0, 0, 0, 256, 0, 0, 0, 0,
+                                 (const void*)pack_fp4_tiles_kernel};
+const KernelInfo kInfoPackFp4Scales = {"pack_fp4_scale_tiles_kernel", "fgg_pack_fp4_weights", 0, 0, 0, 256, 0, 0, 0,
+                                       0, (const void*)pack_fp4_scale_tiles_kernel};
+
 void fp4_tiled_bytes(int32_t G, int64_t N, int64_t K, size_t* b_bytes, size_t* s_bytes) {
   *b_bytes = (size_t)G * (size_t)N * (size_t)(K / 2);
   *s_bytes = (size_t)G * (size_t)(N / 16) * (size_t)((K / 32 + 15) / 16) * 256;
@@ -440,6 +457,8 @@ hipError_t launch_pack_fp4(int32_t G, int64_t N, int64_t K, const uint8_t* b, co
   int64_t g1 = (pieces + 255) / 256, g2 = (rows_spans + 255) / 256;
   if (g1 > cap) g1 = cap;
   if (g2 > cap) g2 = cap;
+  trace_launch(kInfoPackFp4, dim3((unsigned)g1), "G=%d N=%lld K=%lld", (int)G, (long long)N, (long long)K);
+  trace_launch(kInfoPackFp4Scales, dim3((unsigned)g2), "G=%d N=%lld K=%lld", (int)G, (long long)N, (long long)K);
   hipLaunchKernelGGL(pack_fp4_tiles_kernel, dim3((unsigned)g1), dim3(256), 0, stream, b, bt, pieces, K);
   hipLaunchKernelGGL(pack_fp4_scale_tiles_kernel, dim3((unsigned)g2), dim3(256), 0, stream, s, st, rows_spans, K);
   return hipGetLastError();

@@ -368,6 +368,13 @@ size_t w4a4_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t rank) {
   return b;
 }
 
+const KernelInfo kInfoW4a4Prep = {"w4a4_prep_kernel", "fgg_scaled_gemm (W4A4)", 16, 32, 0, 256, 0, 0,
+                                  kLrWaves * 32 * 32 * 2 + kLrWaves * 2 * 64 * 16,
+                                  kLrWaves * 32 * 32 * 2 + kLrWaves * 2 * 64 * 16, (const void*)w4a4_prep_kernel};
+const KernelInfo kInfoW4a4Gemm = {"w4a4_gemm_kernel", "fgg_scaled_gemm (W4A4)", w4::BM, w4::BN, w4::BK,
+                                  64 * w4::kWaves, w4::kStages, w4::kStageBytes, 0, w4::kStages * w4::kStageBytes,
+                                  (const void*)w4a4_gemm_kernel};
+
 hipError_t launch_w4a4(int64_t M, int64_t N, int64_t K, const uint8_t* a, const float* sa,
                        const uint8_t* b, const float* sb, const uint16_t* x_bf16,
                        const uint16_t* l_down, const uint16_t* l_up, int32_t rank,
@@ -384,10 +391,14 @@ hipError_t launch_w4a4(int64_t M, int64_t N, int64_t K, const uint8_t* a, const 
   const int64_t per = 256 * kItems;
   const int64_t lr_blocks = rank > 0 ? (M + 15) / 16 : 0;
   const int64_t blocks = lr_blocks + (na + per - 1) / per + (nb + per - 1) / per;
+  trace_launch(kInfoW4a4Prep, dim3((unsigned)blocks), "M=%lld N=%lld K=%lld rank=%d (%lld low-rank blocks)",
+               (long long)M, (long long)N, (long long)K, (int)rank, (long long)lr_blocks);
   hipLaunchKernelGGL(w4a4_prep_kernel, dim3((unsigned)blocks), dim3(256), 0, st, a, sa, na, Ah, b, sb, nb, Bh,
                      x_bf16, l_down, rank > 0 ? T : nullptr, M, K, lr_blocks);
   const int64_t tiles = ((M + w4::BM - 1) / w4::BM) * ((N + w4::BN - 1) / w4::BN);
   const int64_t grid = (tiles + 7) / 8 * 8;          // a multiple of the XCD count (tile order above)
+  trace_launch(kInfoW4a4Gemm, dim3((unsigned)grid), "M=%lld N=%lld K=%lld%s", (long long)M, (long long)N,
+               (long long)K, bias ? " bias" : "");
   hipLaunchKernelGGL(w4a4_gemm_kernel, dim3((unsigned)grid), dim3(64 * w4::kWaves), 0, st, M, N, K, Ah, Bh,
                      rank > 0 ? T : nullptr, l_up, (int)rank, bias, d, ldd);
   return hipGetLastError();

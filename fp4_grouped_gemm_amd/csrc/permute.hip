@@ -151,7 +151,9 @@ __global__ void __launch_bounds__(256) permute_scatter_kernel(const int32_t* __r
     if (e >= 0) {
       int before = running[e] + rank;
       for (int w = 0; w < wave; ++w) before += wave_cnt[w][e];
-      src_to_row[p] = before;
+      // a pair whose row falls at or beyond M_cap (M_cap too small) is reported as
+      // dropped, so no consumer of src_to_row reads past the caller's buffers
+      src_to_row[p] = before < M_cap ? before : -1;
       if (before < M_cap) row_to_src[before] = (int32_t)p;
     } else if (p < pairs) {
       src_to_row[p] = -1;
@@ -332,12 +334,27 @@ __global__ void __launch_bounds__(256) permute_quantize_kernel(const int32_t* __
   }
 }
 
+const KernelInfo kInfoPermuteHist = {"permute_hist_kernel", "fgg_moe_permute, fgg_moe_permute_quantize", 0, 0, 0,
+                                     256, 0, 0, kMaxE * 4, kMaxE * 4, (const void*)permute_hist_kernel};
+const KernelInfo kInfoPermuteScan = {"permute_scan_kernel", "fgg_moe_permute, fgg_moe_permute_quantize", 0, 0, 0,
+                                     256, 0, 0, 16, 16, (const void*)permute_scan_kernel};
+const KernelInfo kInfoPermuteScatter = {"permute_scatter_kernel", "fgg_moe_permute, fgg_moe_permute_quantize", 0, 0,
+                                        0, 256, 0, 0, kMaxE * 4 * 5 + 16, kMaxE * 4 * 5 + 16,
+                                        (const void*)permute_scatter_kernel};
+const KernelInfo kInfoPermuteGather = {"permute_gather_kernel", "fgg_moe_permute", 0, 0, 0, 256, 0, 0, 0, 0,
+                                       (const void*)permute_gather_kernel};
+const KernelInfo kInfoPermuteQuantize = {"permute_quantize_kernel", "fgg_moe_permute_quantize", 1, 128, 128, 256, 0,
+                                         0, 0, 0, (const void*)permute_quantize_kernel<true>};
+const KernelInfo kInfoFill = {"fill_i32_kernel", "fgg_moe_permute (T == 0)", 0, 0, 0, 256, 0, 0, 0, 0,
+                              (const void*)fill_i32_kernel};
+
 hipError_t launch_permute(const int32_t* ids, int64_t T, int32_t k, int32_t E, int32_t align,
                           const uint8_t* xq, const float* xs, int64_t K, int32_t* offsets,
                           int32_t* counts, int32_t* src_to_row, int32_t* row_to_src, uint8_t* a_out,
                           float* sa_out, int64_t M_cap, void* ws, hipStream_t st) {
   const int64_t pairs = T * (int64_t)k;
   if (pairs == 0) {
+    trace_launch(kInfoFill, dim3(1), "T=0 E=%d M_cap=%lld", (int)E, (long long)M_cap);
     hipLaunchKernelGGL(fill_i32_kernel, dim3(1), dim3(256), 0, st, offsets, (int64_t)E + 1, 0);
     hipLaunchKernelGGL(fill_i32_kernel, dim3(1), dim3(256), 0, st, counts, (int64_t)E, 0);
     if (M_cap > 0)
@@ -346,12 +363,17 @@ hipError_t launch_permute(const int32_t* ids, int64_t T, int32_t k, int32_t E, i
   }
   const int64_t nblk = (pairs + kChunk - 1) / kChunk;
   int32_t* hist = reinterpret_cast<int32_t*>(ws);
+  trace_launch(kInfoPermuteHist, dim3((unsigned)nblk), "pairs=%lld E=%d M_cap=%lld", (long long)pairs, (int)E,
+               (long long)M_cap);
+  trace_launch(kInfoPermuteScan, dim3((unsigned)E), "blocks=%lld", (long long)nblk);
+  trace_launch(kInfoPermuteScatter, dim3((unsigned)nblk), "pairs=%lld align=%d", (long long)pairs, (int)align);
   hipLaunchKernelGGL(permute_hist_kernel, dim3((unsigned)nblk), dim3(256), 0, st, ids, pairs, (int)E, nblk, hist,
                      row_to_src, M_cap);
   hipLaunchKernelGGL(permute_scan_kernel, dim3((unsigned)E), dim3(256), 0, st, hist, nblk, counts);
   hipLaunchKernelGGL(permute_scatter_kernel, dim3((unsigned)nblk), dim3(256), 0, st, ids, pairs, (int)E,
                      (int)align, nblk, hist, counts, offsets, src_to_row, row_to_src, M_cap);
   if (xq != nullptr && M_cap > 0) {
+    trace_launch(kInfoPermuteGather, dim3(1024), "K=%lld M_cap=%lld", (long long)K, (long long)M_cap);
     hipLaunchKernelGGL(permute_gather_kernel, dim3(1024), dim3(256), 0, st, offsets, (int)E, (int)k, row_to_src,
                        xq, xs, T, K, a_out, sa_out, M_cap);
   }
@@ -366,6 +388,8 @@ hipError_t launch_permute_quantize(const int32_t* ids, int64_t T, int32_t k, int
                                 row_to_src, nullptr, nullptr, M_cap, ws, st);
   if (e != hipSuccess || T == 0 || M_cap == 0) return e;
   const unsigned grid = (unsigned)(num_cus > 0 ? num_cus * 8 : 2048);
+  trace_launch(kInfoPermuteQuantize, dim3(grid), "T=%lld K=%lld %s M_cap=%lld", (long long)T, (long long)K,
+               bf16 ? "bf16" : "fp32", (long long)M_cap);
   if (bf16)
     hipLaunchKernelGGL(permute_quantize_kernel<true>, dim3(grid), dim3(256), 0, st, offsets, (int)E, (int)k,
                        src_to_row, row_to_src, x, ldx, T, K, a_out, sa_out, M_cap);
@@ -427,9 +451,13 @@ __global__ void __launch_bounds__(256) combine_kernel(const uint16_t* __restrict
   }
 }
 
+const KernelInfo kInfoCombine = {"combine_kernel", "fgg_moe_combine", 0, 0, 0, 256, 0, 0, 0, 0,
+                                 (const void*)combine_kernel};
+
 hipError_t launch_combine(const uint16_t* y, int64_t ldy, const int32_t* src_to_row, const float* w,
                           int64_t T, int32_t k, int64_t N, uint16_t* out, int64_t ldo, hipStream_t st) {
   if (T == 0 || N == 0) return hipSuccess;
+  trace_launch(kInfoCombine, dim3((unsigned)T), "T=%lld k=%d N=%lld", (long long)T, (int)k, (long long)N);
   hipLaunchKernelGGL(combine_kernel, dim3((unsigned)T), dim3(256), 0, st, y, ldy, src_to_row, w, T, (int)k, N, out, ldo);
   return hipGetLastError();
 }

@@ -178,6 +178,18 @@ __global__ void __launch_bounds__(256) quant_e2m1_e8m0_1x32_kernel(const void* _
 }
 
 // ---------------------------------------------------------------------------
+const KernelInfo kInfoQuantE4m3_1x128 = {"quant_e4m3_1x128_kernel", "fgg_quantize_blockwise {E4M3,F32,1,128}",
+                                         1, 128, 128, 256, 0, 0, 0, 0,
+                                         (const void*)quant_e4m3_1x128_kernel<true, false>};
+const KernelInfo kInfoQuantE4m3_128x128 = {"quant_e4m3_128x128_kernel", "fgg_quantize_blockwise {E4M3,F32,128,128}",
+                                           128, 128, 128, 256, 0, 0, 16, 16,
+                                           (const void*)quant_e4m3_128x128_kernel<true>};
+const KernelInfo kInfoQuantE2m1_1x16 = {"quant_e2m1_1x16_kernel", "fgg_quantize_blockwise {E2M1X2,F32,1,16}",
+                                        1, 16, 16, 256, 0, 0, 0, 0, (const void*)quant_e2m1_1x16_kernel<true>};
+const KernelInfo kInfoQuantE2m1E8m0_1x32 = {"quant_e2m1_e8m0_1x32_kernel",
+                                            "fgg_quantize_blockwise {E2M1X2,E8M0,1,32}", 1, 32, 32, 256, 0, 0, 0, 0,
+                                            (const void*)quant_e2m1_e8m0_1x32_kernel<true>};
+
 hipError_t launch_quantize(const void* x, bool bf16, int64_t rows, int64_t cols, int64_t ldx,
                            QuantKind kind, bool silu, const int32_t* rows_dev, void* q, void* scales,
                            int num_cus, hipStream_t st) {
@@ -190,6 +202,8 @@ hipError_t launch_quantize(const void* x, bool bf16, int64_t rows, int64_t cols,
       const int64_t cap = (int64_t)(num_cus > 0 ? num_cus : 256) * 16;
       if (blocks > cap) blocks = cap;
       dim3 grid((unsigned)blocks);
+      trace_launch(kInfoQuantE4m3_1x128, grid, "rows=%lld cols=%lld %s%s", (long long)rows, (long long)cols,
+                   bf16 ? "bf16" : "fp32", silu ? " silu_mul" : "");
       if (bf16) {
         if (silu) hipLaunchKernelGGL((quant_e4m3_1x128_kernel<true, true>), grid, dim3(256), 0, st, x, rows, cols, ldx, rows_dev, (uint8_t*)q, (float*)scales);
         else hipLaunchKernelGGL((quant_e4m3_1x128_kernel<true, false>), grid, dim3(256), 0, st, x, rows, cols, ldx, rows_dev, (uint8_t*)q, (float*)scales);
@@ -201,18 +215,21 @@ hipError_t launch_quantize(const void* x, bool bf16, int64_t rows, int64_t cols,
     }
     case QuantKind::E4M3_128x128: {
       dim3 grid((unsigned)((rows / 128) * (cols / 128)));
+      trace_launch(kInfoQuantE4m3_128x128, grid, "rows=%lld cols=%lld", (long long)rows, (long long)cols);
       if (bf16) hipLaunchKernelGGL((quant_e4m3_128x128_kernel<true>), grid, dim3(256), 0, st, x, rows, cols, ldx, (uint8_t*)q, (float*)scales);
       else hipLaunchKernelGGL((quant_e4m3_128x128_kernel<false>), grid, dim3(256), 0, st, x, rows, cols, ldx, (uint8_t*)q, (float*)scales);
       break;
     }
     case QuantKind::E2M1_1x16: {
       dim3 grid((unsigned)((rows * (cols / 16) + 255) / 256));
+      trace_launch(kInfoQuantE2m1_1x16, grid, "rows=%lld cols=%lld", (long long)rows, (long long)cols);
       if (bf16) hipLaunchKernelGGL((quant_e2m1_1x16_kernel<true>), grid, dim3(256), 0, st, x, rows, cols, ldx, (uint8_t*)q, (float*)scales);
       else hipLaunchKernelGGL((quant_e2m1_1x16_kernel<false>), grid, dim3(256), 0, st, x, rows, cols, ldx, (uint8_t*)q, (float*)scales);
       break;
     }
     case QuantKind::E2M1_E8M0_1x32: {
       dim3 grid((unsigned)((rows * (cols / 32) + 255) / 256));
+      trace_launch(kInfoQuantE2m1E8m0_1x32, grid, "rows=%lld cols=%lld", (long long)rows, (long long)cols);
       if (bf16) hipLaunchKernelGGL((quant_e2m1_e8m0_1x32_kernel<true>), grid, dim3(256), 0, st, x, rows, cols, ldx, (uint8_t*)q, (uint8_t*)scales);
       else hipLaunchKernelGGL((quant_e2m1_e8m0_1x32_kernel<false>), grid, dim3(256), 0, st, x, rows, cols, ldx, (uint8_t*)q, (uint8_t*)scales);
       break;

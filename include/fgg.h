@@ -93,6 +93,39 @@ int fgg_last_hip_error(void);
 fgg_status fgg_set_num_cus(int n);
 
 /*
+ * Kernel table and launch trace ([MegaMoE] §4.2 prints each generated kernel's
+ * configuration under a debug environment flag; [W4A4] §6 traces a throughput
+ * loss to a shared-memory budget that left one buffer out, and asks for every
+ * stage and buffer choice to be tabulated and checked).
+ *
+ * With the environment variable FGG_DEBUG set (not "0") when the library first
+ * launches, every kernel launch prints one line on stderr: the kernel, the
+ * problem (shape, dtype, options), grid, threads, workgroup tile and LDS budget.
+ *
+ * fgg_kernel_count / fgg_kernel_info_get describe every kernel of the library:
+ * lds_bytes = stages * stage_bytes + other_bytes is the static LDS the kernel
+ * declares (at most 160 KiB, the LDS of one gfx950 compute unit).  The strings
+ * are static and owned by the library.  fgg_kernel_compiled_lds asks the HIP
+ * runtime for the compiled kernel's static LDS (needs a gfx950 device; else
+ * FGG_ERR_UNSUPPORTED).  An index outside [0, fgg_kernel_count()) or a NULL
+ * output is FGG_ERR_INVALID_VALUE.
+ */
+typedef struct {
+  const char* kernel;    /* kernel instance */
+  const char* entry;     /* the entry point(s) that launch it */
+  int32_t tile_m, tile_n, tile_k; /* workgroup tile (0 where the kernel is not tiled) */
+  int32_t threads;       /* threads per workgroup */
+  int32_t stages;        /* LDS ring stages (0: no ring) */
+  int32_t stage_bytes;   /* LDS bytes per ring stage */
+  int32_t other_bytes;   /* LDS outside the ring: group tables, scale caches, reductions */
+  int32_t lds_bytes;     /* declared static LDS */
+} fgg_kernel_info;
+
+int32_t fgg_kernel_count(void);
+fgg_status fgg_kernel_info_get(int32_t i, fgg_kernel_info* info);
+fgg_status fgg_kernel_compiled_lds(int32_t i, int64_t* bytes);
+
+/*
  * fgg_quantize_blockwise — online/offline block quantization.
  *
  * [Infra] Q "量化矩阵乘的维度和流程": every block shares one scale and the code
@@ -142,9 +175,11 @@ fgg_status fgg_quantize_blockwise(const void* x, fgg_dtype x_dtype, int64_t rows
  *   a_out[r][:]   = xq[p / k][:]  (e4m3 codes, K bytes per row), 0 for padding rows
  *   sa_out[kb][r] = xs[kb][p / k] (1×128 scales, K-block-major), 0 for padding rows
  * Rows in [M_total, M_cap) of a_out/sa_out are not written.  If M_total > M_cap
- * (M_cap too small) no row at or beyond M_cap is written and offsets[E] still
- * reports M_total, so the caller can detect it.  M_cap = T·k + E·(align-1) is
- * always enough.
+ * (M_cap too small) no row at or beyond M_cap is written, a pair whose row would
+ * be at or beyond M_cap gets src_to_row = -1 (dropped, so moe_combine never reads
+ * past the GEMM output), and offsets[E] still reports M_total; the grouped GEMMs
+ * called with M = M_cap stop at row M_cap.  M_cap = T·k + E·(align-1) is always
+ * enough.
  *
  * topk_ids: [T][k] int32.  xq: [T][K] e4m3 codes or NULL (index-only mode).
  * xs: [K/128][T] fp32 (ignored when xq is NULL).  K % 128 == 0.
@@ -194,8 +229,8 @@ fgg_status fgg_moe_permute_quantize(const int32_t* topk_ids, int64_t T, int32_t 
  * FGG_LAYOUT_CONTIGUOUS (prefill): rows [offsets[g], offsets[g+1]) of A use
  *   expert g; M is the row count of A, sA and D (e.g. M_cap of the permute);
  *   every offsets[g] must be a multiple of 128 (moe_permute with align 128
- *   guarantees it) and offsets[G] <= M.  Rows >= offsets[G] are not read
- *   or written.  masked_m is optional here (NULL: every row of a segment is
+ *   guarantees it).  Rows >= min(offsets[G], M) are not read or written
+ *   (offsets[G] > M happens when the permute's M_cap was too small).  masked_m is optional here (NULL: every row of a segment is
  *   computed); when given, masked_m[g] (clamped to [0, segment length]) is
  *   group g's number of real rows, e.g. the permute's counts, and the rows
  *   [offsets[g] + masked_m[g], offsets[g+1]) are padding: not written, and
@@ -234,8 +269,15 @@ fgg_status fgg_grouped_gemm_scaled(fgg_layout layout, int32_t G, int64_t M, int6
  * fgg_grouped_gemm_scaled CONTIGUOUS.  For every row r < offsets[G]:
  *   h[r][n] = Σ_kb sA[kb][r] · sB[g][n/128][kb] · Σ_{k in kb} A[r][k]·B[g][n][k]   (fp32, not rounded)
  *   a[r][c] = h[r][c] / (1 + e^-h[r][c]) · h[r][I + c]
- *   q_out[r][c], s_out[c/128][r] = the 1x128 e4m3 quantization of a (the rule of
- *   fgg_quantize_blockwise: s = max|a| / 448 per 128 columns, codes = RNE(a / s))
+ *   s_out[c/128][r] = max|a| / 448 over the 128 columns (1 if all are zero)
+ *   q_out[r][c]     = e4m3_rne_satfinite(a · rcp(s))
+ * All of this runs in fp32 on the accumulators with the hardware base-2
+ * exponential and reciprocal (a few ulps each), so it is not the bit-exact rule
+ * of fgg_quantize_blockwise (RNE of the IEEE quotient a / s): a value within a
+ * few ulps of an e4m3 rounding midpoint may take the neighbouring code.  Against
+ * the exact fp64 chain the scales agree to 2e-4 relative, >= 99.5 % of the codes
+ * are equal, and each dequantized value lies within 2^-3·|a| + 2^-9·s +
+ * 1e-2·(|a| + rms(a)) of the exact SiLU(gate)·up.
  * q_out is [M][I] bytes, s_out [I/128][M] fp32 (K-block-major, the activation
  * layout of the down GEMM).  Rows >= offsets[G] are not written.  counts
  * (optional, [G] int32) has the meaning of masked_m in fgg_grouped_gemm_scaled
@@ -289,6 +331,11 @@ fgg_status fgg_pack_fp4_weights(const void* b, const void* b_scales, int32_t G, 
  *   The operands are dequantized once to fp16 (x·s rounded once) into the
  *   workspace and contracted with fp16 MFMA in fp32; the rank-32 intermediate
  *   x_bf16 · l_down is accumulated in fp32 (bf16 MFMA) and rounded to bf16.
+ *   Range: fp16 holds magnitudes up to 65504, so every dequantized value
+ *   |code · s| <= 6·s must fit: a 16-element group whose largest magnitude is
+ *   at or above 65520 (s >= 10920) would become inf, and values below 2^-24
+ *   flush to zero.  The call checks nothing of this on the device (it would
+ *   need a pass over the scales).
  *   Requires M % 128 == 0, K % 128 == 0, 128 <= K <= 2^22, N % 128 == 0, rank in {0, 32}.
  *   workspace (256-byte aligned) must hold fgg_scaled_gemm_workspace() bytes:
  *   the fp16 copies of A and B, and with a low-rank branch the [M][32]

@@ -192,3 +192,52 @@ def test_permute_quantize_small_m_cap_and_zero_tokens():
     assert np.array_equal(a[:100], aq_r[np.arange(100) // 2])
     got0 = fgg.moe_permute(cuda(np.zeros((0, 4), np.int32)), 3, 128, x=torch.zeros((0, 256), device="cuda"))
     assert to_np(got0["offsets"]).tolist() == [0, 0, 0, 0]
+
+
+def test_undersized_m_cap_nothing_beyond_it():
+    """M_cap smaller than the routed rows need: pairs whose row would be at or past
+    M_cap are reported as dropped (src_to_row = -1), the grouped GEMMs called with
+    M = M_cap stop at row M_cap (guard rows after the output stay untouched), and the
+    combine of those outputs is the oracle's combine without the dropped pairs."""
+    T, k, E, K, N, I = 200, 2, 3, 256, 256, 128
+    g = synth.rng(55)
+    ids = g.integers(0, E, size=(T, k)).astype(np.int32)
+    ref = oracle.moe_permute(ids, E, 128)
+    offsets = ref["offsets"]
+    m_cap = int(offsets[1]) + 50                  # inside expert 1's segment; expert 2 lies beyond
+    assert m_cap < int(offsets[-1]) - 128
+    x = synth.normal(g, (T, K))
+    out = fgg.moe_permute_outputs(T, k, E, 128, K, m_cap=m_cap)
+    perm = fgg.moe_permute(cuda(ids), E, 128, x=cuda(x), out=out)
+    s2r = ref["src_to_row"].copy()
+    s2r[s2r >= m_cap] = -1
+    assert np.array_equal(to_np(perm["offsets"]), offsets)            # the true total is still reported
+    assert np.array_equal(to_np(perm["src_to_row"]), s2r)
+    assert np.array_equal(to_np(perm["row_to_src"]), ref["row_to_src"][:m_cap])
+    w = synth.normal(g, (E, N, K), 0.02)
+    bq = torch.stack([fgg.quantize_blockwise(cuda(w[e]), fgg.Q_E4M3_128x128)[0] for e in range(E)])
+    sb = torch.stack([fgg.quantize_blockwise(cuda(w[e]), fgg.Q_E4M3_128x128)[1] for e in range(E)])
+    guard = torch.full((m_cap + 64, N), float("nan"), dtype=torch.bfloat16, device="cuda")
+    fgg.grouped_gemm_scaled(perm["a"], perm["sa"], bq, sb, offsets=perm["offsets"], out=guard[:m_cap])
+    y = to_np(guard)
+    assert np.all(np.isnan(y[m_cap:]))
+    aq_r, sa_r = oracle.quantize_e4m3_blocks(x, 1, 128)
+    a_r, s_r = oracle.gather_permuted(ref["row_to_src"], int(offsets[-1]), k, aq_r, sa_r)
+    bq_r = np.stack([oracle.quantize_e4m3_blocks(w[e], 128, 128)[0] for e in range(E)])
+    sb_r = np.stack([oracle.quantize_e4m3_blocks(w[e], 128, 128)[1] for e in range(E)])
+    y_ref = oracle.round_bf16(oracle.grouped_gemm_contiguous(a_r, s_r, bq_r, sb_r, offsets, rows=np.arange(m_cap)))
+    tol_check(y[:m_cap], y_ref, what="grouped GEMM with M = M_cap")
+    # the SiLU requant instance: codes and scales stop at row M_cap too
+    wgu = synth.normal(g, (E, 2 * I, K), 0.02)
+    bq2 = torch.stack([fgg.quantize_blockwise(cuda(wgu[e]), fgg.Q_E4M3_128x128)[0] for e in range(E)])
+    sb2 = torch.stack([fgg.quantize_blockwise(cuda(wgu[e]), fgg.Q_E4M3_128x128)[1] for e in range(E)])
+    qg = torch.full((m_cap + 64, I), 0xAB, dtype=torch.uint8, device="cuda")
+    sg = torch.full(((I // 128) * m_cap + 64,), -3.0, dtype=torch.float32, device="cuda")
+    fgg.grouped_gemm_silu_quantize(perm["a"], perm["sa"], bq2, sb2, perm["offsets"], out=qg[:m_cap],
+                                   scales=sg[:(I // 128) * m_cap].view(I // 128, m_cap))
+    assert np.all(to_np(qg)[m_cap:] == 0xAB) and np.all(to_np(sg)[(I // 128) * m_cap:] == -3.0)
+    # combine over the GEMM output of M_cap rows
+    tw = g.random((T, k)).astype(np.float32)
+    got = fgg.moe_combine(guard[:m_cap], perm["src_to_row"], cuda(tw))
+    ref_out = oracle.round_bf16(oracle.moe_combine(y_ref, s2r, tw, T, k))
+    tol_check(to_np(got), ref_out, what="combine with dropped pairs past M_cap")
