@@ -1,6 +1,19 @@
 """Helpers shared by the tests (no arithmetic of the method here)."""
+import concurrent.futures
+import os
+
 import numpy as np
 import torch
+
+
+def pmap(fn, items, workers=None):
+    """[fn(x) for x in items] on a thread pool (numpy releases the GIL in its array
+    loops and BLAS calls), at most 16 threads: the oracle's full-size checks run
+    expert by expert or row block by row block side by side."""
+    items = list(items)
+    n = workers or min(16, len(os.sched_getaffinity(0)), max(len(items), 1))
+    with concurrent.futures.ThreadPoolExecutor(n) as ex:
+        return list(ex.map(fn, items))
 
 
 def tol_check(y, y_ref, rel=1e-2, what=""):
@@ -47,7 +60,12 @@ def codes_close(q, q_ref, s, s_ref, rtol, min_equal=0.999, max_step=1, what=""):
     mism = ~same
     if mism.any():
         a, b = q[mism].astype(int), q_ref[mism].astype(int)
-        zero = ((a & 0x7F) == 0) | ((b & 0x7F) == 0)
-        assert np.all(((a & 0x80) == (b & 0x80)) | zero), f"{what}: sign flips"
+        # across zero: a zero code on either side, or both codes within the e4m3 subnormal
+        # range (|value| < 2^-6 of the scale's 448), where the matrix core's block sums
+        # (accurate to ~1e-4 of the sum of |products|) can move a value across zero
+        zero = ((a & 0x7F) == 0) | ((b & 0x7F) == 0) | (((a & 0x7F) < 8) & ((b & 0x7F) < 8))
+        flip = ~(((a & 0x80) == (b & 0x80)) | zero)
+        assert not flip.any(), (f"{what}: {int(flip.sum())} sign flips of {q.size} codes, e.g. "
+                                f"{list(zip(a[flip][:8].tolist(), b[flip][:8].tolist()))}")
         if max_step is not None:
             assert np.all(np.abs((a & 0x7F) - (b & 0x7F)) <= max_step), f"{what}: codes more than {max_step} step apart"

@@ -3,8 +3,10 @@
 Tolerance (floating point): |y - y_ref| <= 1e-2 · (|y_ref| + rms(y_ref)), with
 y_ref the oracle's fp64 result rounded to bf16.  Padding rows must be exactly
 zero; one group must equal the dense call bit for bit; runs are deterministic.
-Small cases compare every output; the full-size cases compare sampled rows
-(all columns) that the oracle computes one by one."""
+Every test compares every output it checks: the small cases, the persistent
+multi-tile cases (test_gpu_persistent.py) and the full-size dense, decode and
+W4A4 shapes (the oracle runs expert by expert or row block by row block on a
+thread pool); the full prefill chain is in test_gpu_prefill_chain.py."""
 
 import numpy as np
 import pytest
@@ -14,7 +16,7 @@ import fp4_grouped_gemm_amd as fgg
 import oracle
 import synth
 from oracle import formats as F
-from _util import codes_close, cuda, to_np, tol_check
+from _util import codes_close, cuda, pmap, to_np, tol_check
 
 pytestmark = pytest.mark.gpu
 
@@ -239,7 +241,7 @@ def test_dense_small_and_one_group_identity(M, N, K):
         assert torch.equal(y1[:M], y[:M])
 
 
-def test_dense_full_size_sampled_and_deterministic():
+def test_dense_full_size_every_output_and_deterministic():
     w = synth.dense()
     M, N, K = w["M"], w["N"], w["K"]
     xq, xs = fgg.quantize_blockwise(cuda(w["x"]), fgg.Q_E4M3_1x128)
@@ -247,12 +249,11 @@ def test_dense_full_size_sampled_and_deterministic():
     y = fgg.scaled_gemm(xq, xs, bq, sb)
     y2 = fgg.scaled_gemm(xq, xs, bq, sb)
     assert torch.equal(y, y2)
-    rows = np.array([0, 1, 127, 128, 2047, 2100, 4000, 4095])
-    aq_r, sa_r = oracle.quantize_e4m3_blocks(w["x"][rows], 1, 128)
+    aq_r, sa_r = oracle.quantize_e4m3_blocks(w["x"], 1, 128)
     bq_r, sb_r = oracle.quantize_e4m3_blocks(w["w"], 128, 128)
-    assert np.array_equal(to_np(xq)[rows], aq_r) and np.array_equal(to_np(bq), bq_r)
+    assert np.array_equal(to_np(xq), aq_r) and np.array_equal(to_np(bq), bq_r)
     ref = oracle.round_bf16(oracle.scaled_gemm_dense(aq_r, sa_r, bq_r, sb_r))
-    tol_check(to_np(y)[rows], ref, what="dense 4096x4096x7168 sampled rows")
+    tol_check(to_np(y), ref, what="dense 4096x4096x7168, every output")
 
 
 # ------------------------------------------------------------- MoE chains
@@ -398,33 +399,41 @@ def test_masked_fp4_small(G, M, N, K, masked):
         assert np.all(np.isnan(y[e, m:]))                       # rows >= masked_m untouched
 
 
-def test_masked_fp4_full_size_sampled():
+def test_masked_fp4_full_size_every_output():
+    """Decode shape (32 experts x 1..16 rows, N 4096, K 7168): every expert's every
+    real row against the oracle; rows >= masked_m are never written."""
     wl = synth.moe_decode(with_weights=False)
     G, M, N, K = wl["G"], wl["M_max"], wl["N"], wl["K"]
     mm = wl["masked_m"]
     aq, sa = _quant_masked_a_gpu(wl["x"])
     bq = torch.empty((G, N, K // 2), dtype=torch.uint8, device="cuda")
     be = torch.empty((G, N, K // 32), dtype=torch.uint8, device="cuda")
-    keep = {}
     for e in range(G):
-        we = synth.moe_decode_expert_weight(1004, e, N, K)
-        fgg.quantize_blockwise(cuda(we), fgg.Q_E2M1_E8M0_1x32, out=bq[e], scales=be[e])
-        if e in (0, 13, 31):
-            keep[e] = we
-    y = fgg.grouped_gemm_scaled(aq, sa, bq, be, masked_m=cuda(mm), b_qdesc=fgg.Q_E2M1_E8M0_1x32)
+        fgg.quantize_blockwise(cuda(synth.moe_decode_expert_weight(1004, e, N, K)), fgg.Q_E2M1_E8M0_1x32,
+                               out=bq[e], scales=be[e])
+    d = torch.full((G, M, N), float("nan"), dtype=torch.bfloat16, device="cuda")
+    fgg.grouped_gemm_scaled(aq, sa, bq, be, masked_m=cuda(mm), b_qdesc=fgg.Q_E2M1_E8M0_1x32, out=d)
     y2 = fgg.grouped_gemm_scaled(aq, sa, bq, be, masked_m=cuda(mm), b_qdesc=fgg.Q_E2M1_E8M0_1x32)
-    for e in range(G):                     # rows >= masked_m are never written: compare the rest
-        assert torch.equal(y[e, :int(mm[e])], y2[e, :int(mm[e])])
-    y = to_np(y)
-    for e, we in keep.items():
+    for e in range(G):
+        assert torch.equal(d[e, :int(mm[e])], y2[e, :int(mm[e])])
+    y, bq_np, be_np = to_np(d), to_np(bq), to_np(be)
+
+    def expert(e):
         m = int(mm[e])
         aq_r, sa_r = oracle.quantize_e4m3_blocks(wl["x"][e], 1, 128)
-        bc, be_r = oracle.quantize_e2m1_e8m0_groups(we, 32)
+        bc, be_r = oracle.quantize_e2m1_e8m0_groups(synth.moe_decode_expert_weight(1004, e, N, K), 32)
         bp_r = F.pack_e2m1x2(bc)
-        assert np.array_equal(to_np(bq[e]), bp_r)
+        codes_ok = np.array_equal(bq_np[e], bp_r) and np.array_equal(be_np[e], be_r)
         ref = oracle.round_bf16(oracle.grouped_gemm_masked(aq_r[None], sa_r[None], bp_r[None], be_r[None],
                                                            np.array([m])))
-        tol_check(y[e, :m], ref[0, :m], what=f"decode expert {e}")
+        return codes_ok, ref[0, :m]
+
+    res = pmap(expert, range(G))
+    assert all(ok for ok, _ in res), "decode weight codes differ from the oracle's"
+    tol_check(np.concatenate([y[e, :int(mm[e])] for e in range(G)]), np.concatenate([r for _, r in res]),
+              what="decode 32 experts, every output")
+    for e in range(G):
+        assert np.all(np.isnan(y[e, int(mm[e]):]))
 
 
 @pytest.mark.parametrize("G,M,N,K,masked", [(3, 16, 256, 1024, [16, 0, 9]), (2, 7, 128, 384, [7, 3]),
@@ -509,9 +518,11 @@ def _w4a4_run(wl, rows=None):
     qx_r, sx_r = oracle.quantize_e2m1_fp32_groups(wl["x"][rows], 16)
     qw_r, sw_r = oracle.quantize_e2m1_fp32_groups(wl["w"], 16)
     assert np.array_equal(to_np(xq)[rows], F.pack_e2m1x2(qx_r)) and np.array_equal(to_np(wq), F.pack_e2m1x2(qw_r))
-    ref = oracle.round_bf16(oracle.w4a4_lowrank_gemm(qx_r, sx_r, qw_r, sw_r, wl["x"][rows], wl["l_down"],
-                                                     wl["l_up"], wl["bias"]))
-    return to_np(y)[rows], ref
+    # the oracle in 256-row blocks side by side
+    blocks = [slice(r, r + 256) for r in range(0, len(rows), 256)]
+    ref = np.concatenate(pmap(lambda b: oracle.w4a4_lowrank_gemm(
+        qx_r[b], sx_r[b], qw_r, sw_r, wl["x"][rows][b], wl["l_down"], wl["l_up"], wl["bias"]), blocks))
+    return to_np(y)[rows], oracle.round_bf16(ref)
 
 
 def test_w4a4_small():
@@ -544,10 +555,10 @@ def test_w4a4_no_epilogue():
     tol_check(y, ref, what="w4a4 without epilogue")
 
 
-def test_w4a4_full_size_sampled():
+def test_w4a4_full_size_every_output():
     wl = synth.w4a4()
-    y, ref = _w4a4_run(wl, rows=np.array([0, 1, 63, 64, 1000, 2048, 4000, 4095]))
-    tol_check(y, ref, what="w4a4 4096x3072x3072 sampled rows")
+    y, ref = _w4a4_run(wl)
+    tol_check(y, ref, what="w4a4 4096x3072x3072, every output")
 
 
 @pytest.mark.parametrize("M,N,K", [(128, 256, 384), (256, 128, 3072)])
