@@ -56,6 +56,33 @@ def _sync():
     torch.cuda.synchronize()
 
 
+def roofline_entry(kernel, flops, nbytes, seconds, mfma_peak_tflops, how):
+    """Both roofline fractions of one launch: achieved algorithmic FLOP/s against the
+    matrix-core peak of its dtype and algorithmic bytes/s against HBM.  The bound is
+    the side with the larger minimum time (arithmetic intensity against the ridge
+    peak FLOP/s / peak B/s); "achieved", "peak" and "frac" are on that side."""
+    t_mfma = flops / (mfma_peak_tflops * 1e12) if flops else 0.0
+    t_hbm = nbytes / (PEAK_HBM_GBS * 1e9)
+    tf = flops / seconds / 1e12
+    gbs = nbytes / seconds / 1e9
+    hbm = t_hbm >= t_mfma
+    return {
+        "kernel": kernel,
+        "bound": "hbm" if hbm else "mfma",
+        "achieved": round(gbs, 1) if hbm else round(tf, 1),
+        "peak": PEAK_HBM_GBS if hbm else mfma_peak_tflops,
+        "unit": "GB/s" if hbm else "TFLOP/s",
+        "frac": round(gbs / PEAK_HBM_GBS if hbm else tf / mfma_peak_tflops, 4),
+        "us_per_launch": round(seconds * 1e6, 2),
+        "algorithmic_flop": flops, "algorithmic_bytes": nbytes,
+        "intensity_flop_per_byte": round(flops / nbytes, 1),
+        "ridge_flop_per_byte": round(mfma_peak_tflops * 1e12 / (PEAK_HBM_GBS * 1e9), 1),
+        "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
+        "mfma_frac": round(tf / mfma_peak_tflops, 4) if flops else None,
+        "algorithmic": how,
+    }
+
+
 HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000   # hipEventDisableSystemFence (hip_runtime_api.h)
 
 
@@ -126,7 +153,16 @@ class StepMarks:
 
 # ----------------------------------------------------------------- prefill
 
-def setup_prefill(fgg, synth, torch):
+def bench_weight(synth, which, e, n, kk):
+    """Expert e's fp32 weights of the benched layer ("gu" or "dn"), N(0, 0.02), drawn on
+    the device from a seeded generator (fast for the 32 large experts)."""
+    return synth.normal_cuda((31_000 if which == "gu" else 32_000) + e, (n, kk), 0.02)
+
+
+def setup_prefill(fgg, synth, torch, weight_fn=None):
+    """Inputs of the prefill step resident in HBM.  weight_fn(which, e, N, K) gives
+    expert e's fp32 weights ("gu" [N_gu, K] or "dn" [N_dn, K_dn]) as a device
+    tensor; by default they are drawn on the device (synth.normal_cuda, N(0, 0.02))."""
     cfg = synth.MOE_PREFILL
     T, K, E, k = cfg["T"], cfg["K"], cfg["E"], cfg["k"]
     Ngu, Ndn, Kdn = cfg["N_gu"], cfg["N_dn"], cfg["K_dn"]
@@ -138,10 +174,13 @@ def setup_prefill(fgg, synth, torch):
     gu_s = torch.empty((E, Ngu // 128, K // 128), dtype=torch.float32, device="cuda")
     dn_q = torch.empty((E, Ndn, Kdn), dtype=torch.uint8, device="cuda")
     dn_s = torch.empty((E, Ndn // 128, Kdn // 128), dtype=torch.float32, device="cuda")
+    if weight_fn is None:
+        def weight_fn(which, e, n, kk):
+            return bench_weight(synth, which, e, n, kk)
     for e in range(E):      # offline weight quantization (untimed)
-        w = synth.normal_cuda(31_000 + e, (Ngu, K), 0.02)
+        w = weight_fn("gu", e, Ngu, K)
         fgg.quantize_blockwise(w, fgg.Q_E4M3_128x128, out=gu_q[e], scales=gu_s[e])
-        w = synth.normal_cuda(32_000 + e, (Ndn, Kdn), 0.02)
+        w = weight_fn("dn", e, Ndn, Kdn)
         fgg.quantize_blockwise(w, fgg.Q_E4M3_128x128, out=dn_q[e], scales=dn_s[e])
     del w
     perm = fgg.moe_permute_outputs(T, k, E, 128, K)
@@ -220,10 +259,16 @@ def bench_decode(fgg, synth, torch, iters=50, copies=3):
                                                       b_qdesc=fgg.Q_E2M1_E8M0_1x32_TILED, out=d, n=N), iters, 5)
     wbytes = G * N * (K // 2) + G * N * (K // 32)
     gbs = wbytes / (ms * 1e-3) / 1e9
+    rows = int(wl["masked_m"].sum())
+    flops = 2.0 * rows * N * K
+    nbytes = wbytes + rows * K * (1 + 4 / 128) + rows * N * 2
+    roof = roofline_entry("gemm_masked_fp4_lds_kernel<tiled> (decode masked GEMM)", flops, nbytes, ms * 1e-3,
+                          PEAK_FP4_TFLOPS, "2*%d*%d*%d FLOP; bytes = E2M1 weights + E8M0 scales of 32 experts, "
+                          "the %d real rows' e4m3 codes + scales, their bf16 outputs" % (rows, N, K, rows))
     return dict(workload="moe_decode G=32 M=1..16 (U) N=4096 K=7168 E2M1+E8M0/32 weights (tiled layout), "
                          "e4m3 1x128 acts",
                 us_per_call=round(ms * 1e3, 2), weight_bytes=wbytes, value=round(gbs, 1), unit="GB/s",
-                pct_hbm_peak=round(100 * gbs / PEAK_HBM_GBS, 1))
+                pct_hbm_peak=round(100 * gbs / PEAK_HBM_GBS, 1), roofline=roof)
 
 
 def bench_dense(fgg, synth, torch, iters=30, copies=3):
@@ -260,12 +305,13 @@ def bench_w4a4(fgg, synth, torch, iters=30):
 # ----------------------------------------------------------- CPU baseline
 
 def cpu_baseline(synth, target_s=15.0):
-    """The oracle's MoE layer, expert by expert on the same routing and weights:
-    quantize the expert's tokens (1x128 e4m3), gate-up GEMM (fp64 per-group
-    formula), bf16 output, SiLU(gate)*up requantized, down GEMM, bf16 output
-    and the gate-weighted accumulation into the layer output.  Experts are
-    taken largest first until about target_s seconds of CPU work; weight
-    quantization is offline (untimed) as on the GPU."""
+    """The oracle's MoE layer, expert by expert, on the benched layer's routing,
+    bf16 input and fp32 weights (the same values the GPU step quantizes: copied
+    from the device generator to the host): quantize the expert's tokens (1x128
+    e4m3), gate-up GEMM (fp64 per-group formula), SiLU(gate)*up requantized,
+    down GEMM, bf16 output and the gate-weighted accumulation into the layer
+    output.  Experts are taken largest first until about target_s seconds of
+    CPU work; weight quantization is offline (untimed) as on the GPU."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
@@ -278,21 +324,21 @@ def cpu_baseline(synth, target_s=15.0):
     ids, tw = r["topk_ids"], r["topk_w"]
     counts = np.bincount(ids[ids >= 0], minlength=cfg["E"])
     order = np.argsort(-counts, kind="stable")
-    x = synth.moe_prefill_x()
+    x = synth.to_bf16_values(synth.moe_prefill_x())       # the step's input is bf16
     out = np.zeros((x.shape[0], Ndn))
     flops = 0.0
     elapsed = 0.0
     rows_done = 0
     used = []
     for e in order:
-        wq_gu, ws_gu = oracle.quantize_e4m3_blocks(synth.moe_prefill_expert_weight(1003, "gu", int(e), Ngu, K), 128, 128)
-        wq_dn, ws_dn = oracle.quantize_e4m3_blocks(synth.moe_prefill_expert_weight(1003, "dn", int(e), Ndn, Kdn),
+        wq_gu, ws_gu = oracle.quantize_e4m3_blocks(bench_weight(synth, "gu", int(e), Ngu, K).cpu().numpy(), 128, 128)
+        wq_dn, ws_dn = oracle.quantize_e4m3_blocks(bench_weight(synth, "dn", int(e), Ndn, Kdn).cpu().numpy(),
                                                    128, 128)
         t0 = time.perf_counter()
         toks, slots = np.nonzero(ids == e)
         aq, sa = oracle.quantize_e4m3_blocks(x[toks], 1, 128)
         seg = np.array([0, len(toks)])
-        h = oracle.round_bf16(oracle.grouped_gemm_contiguous(aq, sa, wq_gu[None], ws_gu[None], seg))
+        h = oracle.grouped_gemm_contiguous(aq, sa, wq_gu[None], ws_gu[None], seg)   # fp32 sums fused on the GPU
         a2, s2 = oracle.silu_mul_quantize(h)
         y = oracle.round_bf16(oracle.grouped_gemm_contiguous(a2, s2, wq_dn[None], ws_dn[None], seg))
         out[toks] += tw[toks, slots][:, None] * y
@@ -404,26 +450,33 @@ def main():
             "tflops": round((gu_flops + dn_flops) / ((gu_ms + dn_ms) * 1e-3) / 1e12, 1),
             "useful_gflop": round((gu_flops + dn_flops) / 1e9, 1),
         },
-        "roofline": {
-            "kernel": "gemm_fp8_contig_kernel<SILU> (gate-up grouped GEMM, SiLU requant epilogue)",
-            "bound": "mfma",
-            "achieved": round(gu_tf, 1),
-            "peak": PEAK_FP8_TFLOPS,
-            "unit": "TFLOP/s",
-            "frac": round(gu_tf / PEAK_FP8_TFLOPS, 4),
-            "traffic": measured_traffic(os.path.dirname(os.path.abspath(__file__))),
-            "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE x2 + WRITE_SIZE, copy-calibrated)",
-            "algorithmic": ("2*8192*4096*7168 = %.1f GFLOP per launch; bytes: A codes + scales, B codes + scales, "
-                            "output codes + scales of the routed rows = %.0f MB") % (
-                gu_flops / 1e9,
-                (m_total * cfg["K"] * (1 + 4 / 128)
-                 + cfg["E"] * cfg["N_gu"] * cfg["K"] * (1 + 4 / (128 * 128))
-                 + cfg["T"] * cfg["k"] * cfg["E"] // cfg["E_global"] * (cfg["N_gu"] // 2) * (1 + 4 / 128)) / 1e6),
-        },
+    }
+    # algorithmic bytes: what a kernel that reads every operand byte and writes every
+    # output byte once must move (routed rows only; padding rows carry no data)
+    K, Ngu, Ndn, Kdn, E = cfg["K"], cfg["N_gu"], cfg["N_dn"], cfg["K_dn"], cfg["E"]
+    I = Ngu // 2
+    gu_bytes = (n_local * K * (1 + 4 / 128) + E * Ngu * K * (1 + 4 / (128 * 128)) + n_local * I * (1 + 4 / 128))
+    dn_bytes = (n_local * Kdn * (1 + 4 / 128) + E * Ndn * Kdn * (1 + 4 / (128 * 128)) + n_local * Ndn * 2)
+    gu_roof = roofline_entry(
+        "gemm_fp8_contig_kernel<silu> (gate-up grouped GEMM, SiLU requant epilogue)", gu_flops, gu_bytes,
+        gu_ms * 1e-3, PEAK_FP8_TFLOPS,
+        "2*%d*%d*%d FLOP; bytes = routed rows' e4m3 codes + 1x128 scales, all experts' gate-up weights + "
+        "128x128 scales, requantized output codes + scales" % (n_local, Ngu, K))
+    gu_roof["traffic"] = measured_traffic(os.path.dirname(os.path.abspath(__file__)))
+    gu_roof["traffic_unit"] = "HBM bytes per launch (rocprofv3 FETCH_SIZE x2 + WRITE_SIZE, copy-calibrated)"
+    result["roofline"] = gu_roof
+    result["rooflines"] = {
+        "gate_up": gu_roof,
+        "down": roofline_entry(
+            "gemm_fp8_contig_kernel<plain> (down grouped GEMM)", dn_flops, dn_bytes, dn_ms * 1e-3, PEAK_FP8_TFLOPS,
+            "2*%d*%d*%d FLOP; bytes = routed rows' e4m3 codes + scales, all experts' down weights + scales, "
+            "bf16 outputs of the routed rows" % (n_local, Ndn, Kdn)),
     }
     if not args.no_secondary:
+        dec = bench_decode(fgg, synth, torch)
+        result["rooflines"]["decode"] = dec.pop("roofline")
         result["secondary"] = {
-            "moe_decode": bench_decode(fgg, synth, torch),
+            "moe_decode": dec,
             "dense": bench_dense(fgg, synth, torch),
             "w4a4": bench_w4a4(fgg, synth, torch),
         }

@@ -45,3 +45,15 @@ def test_committed_traffic_record_names_existing_sources():
     for s in rec["sources"]:
         assert os.path.exists(os.path.join(ROOT, s))
     assert rec["fetch_size_kib"] > 0 and rec["write_size_kib"] > 0
+
+
+def test_roofline_bound_follows_intensity():
+    # gate-up-like launch: 481 GFLOP over 1032 MB is 466 FLOP/B, below the FP8 ridge of 625
+    r = bench.roofline_entry("k", 481.0e9, 1032.0e6, 341.32e-6, bench.PEAK_FP8_TFLOPS, "")
+    assert r["bound"] == "hbm" and r["unit"] == "GB/s" and r["peak"] == bench.PEAK_HBM_GBS
+    assert abs(r["frac"] - 1032.0e6 / 341.32e-6 / 8e12) < 1e-4 and r["frac"] == r["hbm_frac"]
+    assert abs(r["mfma_frac"] - 481.0e9 / 341.32e-6 / 5e15) < 1e-4
+    assert r["ridge_flop_per_byte"] == 625.0
+    # dense-like launch: 240.5 GFLOP over 93 MB is far above the ridge
+    r = bench.roofline_entry("k", 240.5e9, 93.0e6, 119e-6, bench.PEAK_FP8_TFLOPS, "")
+    assert r["bound"] == "mfma" and r["unit"] == "TFLOP/s" and r["frac"] == r["mfma_frac"]
