@@ -76,4 +76,5 @@ from .gemm import (  # noqa: F401
     grouped_gemm_masked,
     scaled_gemm_dense,
     w4a4_lowrank_gemm,
+    mxfp4_lowrank_gemm,
 )

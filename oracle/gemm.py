@@ -133,3 +133,34 @@ def w4a4_lowrank_gemm(qx, sx, qw, sw, x_bf16=None, l_down=None, l_up=None, bias=
     if bias is not None:
         y += np.asarray(bias, dtype=np.float64)[None, :]
     return y
+
+
+def mxfp4_lowrank_gemm(qx, ex, qw, ew, x_bf16=None, l_down=None, l_up=None, bias=None, group=32):
+    """The [W4A4] §1 operator Y = (Q(X)·Q(W)ᵀ) ⊙ scale + L(X) + b with Q in the MX
+    form: E2M1 codes and one E8M0 power-of-two scale per 32 elements along K on
+    both operands (the per-32 E8M0 block of the decode weights, here on the
+    activations too), so that ⊙ scale is the pair 2^(ex-127)·2^(ew-127) applied to
+    each 32-element partial sum:
+
+        Y[m, n] = Σ_g  2^(ex[m,g]-127) · 2^(ew[n,g]-127) · Σ_{k in g} dec(qx[m,k]) · dec(qw[n,k])
+                  + (X_bf16 · L_d)[m, :] · L_u[:, n] + b[n]
+
+    qx uint8 [M, K] E2M1 codes (one per byte, unpacked) with ex uint8 [M, K/32];
+    qw uint8 [N, K] with ew uint8 [N, K/32].  Every partial sum and its power-of-two
+    scaling is exact in float64; the low-rank and bias terms are those of
+    w4a4_lowrank_gemm."""
+    qx = np.asarray(qx)
+    qw = np.asarray(qw)
+    M, K = qx.shape
+    sx = decode_e8m0(ex)                                  # [M, K/32] powers of two
+    sw = decode_e8m0(ew)
+    y = np.zeros((M, qw.shape[0]))
+    for g in range(K // group):
+        ks = slice(g * group, (g + 1) * group)
+        y += (decode_e2m1(qx[:, ks]) @ decode_e2m1(qw[:, ks]).T) * sx[:, g:g + 1] * sw[None, :, g]
+    if l_down is not None:
+        xd = np.asarray(x_bf16, dtype=np.float64)
+        y += (xd @ np.asarray(l_down, dtype=np.float64)) @ np.asarray(l_up, dtype=np.float64)
+    if bias is not None:
+        y += np.asarray(bias, dtype=np.float64)[None, :]
+    return y

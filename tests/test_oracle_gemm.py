@@ -188,3 +188,92 @@ def test_w4a4_brute_force_and_branches():
     # the low-rank and bias branches are additive and optional
     y0 = oracle.w4a4_lowrank_gemm(qx, sx, qw, sw)
     np.testing.assert_allclose(y - y0, (x.astype(np.float64) @ ld) @ lu + b, rtol=1e-10, atol=1e-14)
+
+
+# ------------------------------------------------------------ MXFP4 A4W4
+
+def _mx_problem(seed, M, N, K, r=4):
+    g = synth.rng(seed)
+    x = synth.to_bf16_values(synth.normal(g, (M, K)))
+    w = synth.normal(g, (N, K), 0.02)
+    qx, ex = oracle.quantize_e2m1_e8m0_groups(x, 32)
+    qw, ew = oracle.quantize_e2m1_e8m0_groups(w, 32)
+    ld = synth.to_bf16_values(synth.normal(g, (K, r), 0.01))
+    lu = synth.to_bf16_values(synth.normal(g, (r, N), 0.01))
+    b = synth.to_bf16_values(synth.normal(g, (N,), 0.1))
+    return x, w, qx, ex, qw, ew, ld, lu, b
+
+
+def test_mxfp4_brute_force_and_python_loop():
+    M, N, K, r = 24, 40, 128, 4
+    x, w, qx, ex, qw, ew, ld, lu, b = _mx_problem(41, M, N, K, r)
+    y = oracle.mxfp4_lowrank_gemm(qx, ex, qw, ew, x, ld, lu, b)
+    xd = F.decode_e2m1(qx) * np.repeat(np.ldexp(1.0, ex.astype(int) - 127), 32, axis=1)
+    wd = F.decode_e2m1(qw) * np.repeat(np.ldexp(1.0, ew.astype(int) - 127), 32, axis=1)
+    np.testing.assert_allclose(y, xd @ wd.T + (x.astype(np.float64) @ ld) @ lu + b, rtol=1e-12, atol=1e-14)
+    for (i, j) in [(0, 0), (7, 31), (23, 39)]:
+        acc = 0.0
+        for k in range(K):
+            acc += (float(F.E2M1_TABLE[qx[i, k]]) * 2.0 ** (int(ex[i, k // 32]) - 127)
+                    * float(F.E2M1_TABLE[qw[j, k]]) * 2.0 ** (int(ew[j, k // 32]) - 127))
+        for k in range(K):
+            for q in range(r):
+                acc += float(x[i, k]) * float(ld[k, q]) * float(lu[q, j])
+        acc += float(b[j])
+        assert y[i, j] == pytest.approx(acc, rel=1e-12, abs=1e-14)
+
+
+def test_mxfp4_equals_w4a4_with_the_same_scales_as_fp32():
+    """The MX form is the per-group formula with fp32 scales that happen to be
+    powers of two: each E8M0 scale written as an fp32 scale for both 16-element
+    halves of its 32-element group gives the same result through the W4A4 oracle
+    (an independent loop over 16-element groups)."""
+    M, N, K = 16, 24, 256
+    x, w, qx, ex, qw, ew, ld, lu, b = _mx_problem(42, M, N, K)
+    sx16 = np.repeat(np.ldexp(1.0, ex.astype(int) - 127), 2, axis=1).astype(np.float32)
+    sw16 = np.repeat(np.ldexp(1.0, ew.astype(int) - 127), 2, axis=1).astype(np.float32)
+    np.testing.assert_allclose(oracle.mxfp4_lowrank_gemm(qx, ex, qw, ew, x, ld, lu, b),
+                               oracle.w4a4_lowrank_gemm(qx, sx16, qw, sw16, x, ld, lu, b), rtol=1e-13, atol=1e-15)
+
+
+def test_mxfp4_closed_form_and_one_hot_scales():
+    M, N, K = 8, 8, 128
+    # every code 1.5 (E2M1 0x3) against every code -3 (0xD), unit scales: K · 1.5 · -3 exactly
+    qx = np.full((M, K), 0x3, np.uint8)
+    qw = np.full((N, K), 0xD, np.uint8)
+    e1 = np.full((M, K // 32), 127, np.uint8)
+    f1 = np.full((N, K // 32), 127, np.uint8)
+    assert np.all(oracle.mxfp4_lowrank_gemm(qx, e1, qw, f1) == K * 1.5 * -3.0)
+    # one nonzero pair at (m, k) and (n, k): exactly one output, scaled by the two E8M0
+    # bytes of k's 32-group (distinct powers of two per row and group identify them)
+    ex = (120 + np.arange(M * (K // 32)).reshape(M, K // 32) % 13).astype(np.uint8)
+    ew = (125 + np.arange(N * (K // 32)).reshape(N, K // 32) % 7).astype(np.uint8)
+    for (m, n, k) in [(0, 0, 0), (3, 5, 33), (7, 7, 127), (2, 6, 64)]:
+        a = np.zeros((M, K), np.uint8)
+        a[m, k] = 0x2                                  # 1.0
+        bw = np.zeros((N, K), np.uint8)
+        bw[n, k] = 0xF                                 # -6.0
+        y = oracle.mxfp4_lowrank_gemm(a, ex, bw, ew)
+        expect = np.zeros((M, N))
+        expect[m, n] = -6.0 * 2.0 ** (int(ex[m, k // 32]) - 127) * 2.0 ** (int(ew[n, k // 32]) - 127)
+        assert np.array_equal(y, expect), (m, n, k)
+    # raising one row's E8M0 exponents by one doubles that row exactly
+    x, w, qx, ex, qw, ew, *_ = _mx_problem(43, 12, 16, 256)
+    y = oracle.mxfp4_lowrank_gemm(qx, ex, qw, ew)
+    ex2 = ex.copy()
+    ex2[5] += 1
+    y2 = oracle.mxfp4_lowrank_gemm(qx, ex2, qw, ew)
+    assert np.array_equal(y2[5], 2 * y[5]) and np.array_equal(np.delete(y2, 5, 0), np.delete(y, 5, 0))
+
+
+def test_mxfp4_quantized_product_tracks_the_real_product():
+    """Both operands quantized with the never-clipping E8M0 rule: the quantized
+    product differs from the fp64 product of the unquantized operands by the
+    E2M1 rounding only (a few percent of rms), which catches an inverted or
+    misplaced scale (that would be off by powers of two)."""
+    M, N, K = 64, 64, 512
+    x, w, qx, ex, qw, ew, *_ = _mx_problem(44, M, N, K)
+    y = oracle.mxfp4_lowrank_gemm(qx, ex, qw, ew)
+    ref = x.astype(np.float64) @ w.astype(np.float64).T
+    rms = np.sqrt(np.mean(ref ** 2))
+    assert np.sqrt(np.mean((y - ref) ** 2)) < 0.2 * rms
