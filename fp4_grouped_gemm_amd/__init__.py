@@ -16,7 +16,7 @@ __all__ = [
     "FggError", "load_library", "library_path",
     "Q_E4M3_1x128", "Q_E4M3_128x128", "Q_E2M1_1x16", "Q_E2M1_E8M0_1x32", "Q_E2M1_E8M0_1x32_TILED",
     "quantize_blockwise", "moe_permute", "moe_permute_outputs", "moe_permute_workspace_bytes",
-    "grouped_gemm_scaled", "grouped_gemm_silu_quantize", "pack_fp4_weights",
+    "moe_permute_quantize_noalloc", "grouped_gemm_scaled", "grouped_gemm_silu_quantize", "pack_fp4_weights",
     "scaled_gemm", "moe_combine", "set_num_cus", "kernel_table", "kernel_compiled_lds",
 ]
 
@@ -87,6 +87,7 @@ def load_library():
         "fgg_moe_permute_workspace": ([I64, I32, I32, ctypes.POINTER(SZ)], I32),
         "fgg_moe_permute": ([P, I64, I32, I32, I32, P, P, I64, P, P, P, P, P, P, I64, P, SZ, P], I32),
         "fgg_moe_permute_quantize": ([P, I64, I32, I32, I32, P, I32, I64, I64, P, P, P, P, P, P, I64, P, SZ, P], I32),
+        "fgg_moe_permute_quantize_noalloc": ([P, I64, I32, I32, I32, P, I32, I64, I64, P, P, P, P, P, P, I64, P], I32),
         "fgg_grouped_gemm_scaled": ([I32, I32, I64, I64, I64, P, P, QDesc, P, P, QDesc, P, P, P, I64, P], I32),
         "fgg_grouped_gemm_silu_quantize": ([I32, I64, I64, I64, P, P, QDesc, P, P, QDesc, P, P, P, P, P], I32),
         "fgg_scaled_gemm_workspace": ([I64, I64, I64, QDesc, QDesc, ctypes.POINTER(Epilogue), ctypes.POINTER(SZ)], I32),
@@ -257,6 +258,25 @@ def moe_permute(topk_ids: torch.Tensor, num_experts: int, align: int = 128, xq=N
     _check("fgg_moe_permute", st)
     return dict(offsets=offsets, counts=counts, src_to_row=s2r[:T * k], row_to_src=r2s[:m_cap], a=a_out,
                 sa=sa_out, m_cap=m_cap)
+
+
+def moe_permute_quantize_noalloc(topk_ids: torch.Tensor, num_experts: int, x: torch.Tensor, out, align: int = 128):
+    """fgg_moe_permute_quantize_noalloc: the fused permute-quantize with the library's
+    static device scratch instead of a workspace (for callers that cannot allocate).
+    ``out`` (from moe_permute_outputs) receives every output; its workspace is unused."""
+    assert topk_ids.dtype == torch.int32 and topk_ids.dim() == 2 and topk_ids.is_contiguous()
+    assert x.dim() == 2 and x.stride(1) == 1 and x.dtype in (torch.bfloat16, torch.float32)
+    T, k = topk_ids.shape
+    K = x.shape[1]
+    assert out["a"] is not None and out["a"].shape[1] == K
+    st = load_library().fgg_moe_permute_quantize_noalloc(
+        _ptr(topk_ids), T, k, int(num_experts), align, _ptr(x), FGG_BF16 if x.dtype == torch.bfloat16 else FGG_F32,
+        K, x.stride(0), _ptr(out["offsets"]), _ptr(out["counts"]), _ptr(out["src_to_row"]), _ptr(out["row_to_src"]),
+        _ptr(out["a"]), _ptr(out["sa"]), out["m_cap"], _stream(topk_ids.device))
+    _check("fgg_moe_permute_quantize_noalloc", st)
+    m = out["m_cap"]
+    return dict(offsets=out["offsets"], counts=out["counts"], src_to_row=out["src_to_row"][:T * k],
+                row_to_src=out["row_to_src"][:m], a=out["a"], sa=out["sa"], m_cap=m)
 
 
 # --------------------------------------------------------------------- GEMMs

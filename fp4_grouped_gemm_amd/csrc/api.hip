@@ -202,6 +202,24 @@ fgg_status fgg_moe_permute_quantize(const int32_t* topk_ids, int64_t T, int32_t 
                                              workspace, num_cus, (hipStream_t)stream));
 }
 
+fgg_status fgg_moe_permute_quantize_noalloc(const int32_t* topk_ids, int64_t T, int32_t k, int32_t E, int32_t align,
+                                            const void* x, fgg_dtype x_dtype, int64_t K, int64_t ldx,
+                                            int32_t* offsets, int32_t* counts, int32_t* src_to_row,
+                                            int32_t* row_to_src, void* a_out, float* sa_out, int64_t M_cap,
+                                            void* stream) {
+  if (T < 0 || k < 1 || k > 64 || E < 1 || E > 1024) return FGG_ERR_INVALID_VALUE;
+  if (T > 0 && fgg::permute_workspace_bytes(T, k, E) > fgg::kPermuteScratchBytes) return FGG_ERR_UNSUPPORTED;
+  void* ws = nullptr;
+  if (T > 0) {
+    fgg_status st = device_check(nullptr);
+    if (st != FGG_OK) return st;
+    const hipError_t e = fgg::permute_scratch(&ws);
+    if (e != hipSuccess) return hip_fail(e);
+  }
+  return fgg_moe_permute_quantize(topk_ids, T, k, E, align, x, x_dtype, K, ldx, offsets, counts, src_to_row,
+                                  row_to_src, a_out, sa_out, M_cap, ws, fgg::kPermuteScratchBytes, stream);
+}
+
 fgg_status fgg_grouped_gemm_scaled(fgg_layout layout, int32_t G, int64_t M, int64_t N, int64_t K,
                                    const void* a, const void* a_scales, fgg_qdesc aq, const void* b,
                                    const void* b_scales, fgg_qdesc bq, const int32_t* offsets,

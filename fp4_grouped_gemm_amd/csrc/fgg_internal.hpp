@@ -52,6 +52,13 @@ hipError_t launch_permute(const int32_t* ids, int64_t T, int32_t k, int32_t E, i
                           int32_t* counts, int32_t* src_to_row, int32_t* row_to_src, uint8_t* a_out,
                           float* sa_out, int64_t M_cap, void* ws, hipStream_t st);
 
+// The no-allocation permute's scratch: a file-scope device array of this many bytes
+// (holds the permute workspace of up to (kPermuteScratchBytes - 256) / 4 histogram
+// entries, ceil(T·k / 256) · E); permute_scratch gives its device address on the
+// current device (taken once per device).
+constexpr size_t kPermuteScratchBytes = size_t(2) << 20;
+hipError_t permute_scratch(void** ptr);
+
 hipError_t launch_permute_quantize(const int32_t* ids, int64_t T, int32_t k, int32_t E, int32_t align,
                                    const void* x, bool bf16, int64_t K, int64_t ldx, int32_t* offsets,
                                    int32_t* counts, int32_t* src_to_row, int32_t* row_to_src, uint8_t* a_out,

@@ -19,6 +19,8 @@
 //            (stable) plus per-wave and per-block running counts.
 //   gather:  one wave per row of [0, M_total) copies the token's codes (zeros
 //            for padding rows); a second phase writes the K-block-major scales.
+#include <mutex>
+
 #include "fgg_device.hpp"
 #include "fgg_internal.hpp"
 
@@ -378,6 +380,39 @@ hipError_t launch_permute(const int32_t* ids, int64_t T, int32_t k, int32_t E, i
                        xq, xs, T, K, a_out, sa_out, M_cap);
   }
   return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Scratch for callers that cannot allocate (fgg_moe_permute_quantize_noalloc):
+// the per-block expert histograms live in this file-scope device array instead of
+// a caller workspace.  Each device that runs the library holds its own copy for
+// the life of the process; its address is taken per device with
+// hipGetSymbolAddress (the array's name is only a host-side stand-in).  Every
+// histogram entry is written before it is read, so nothing is cleared between
+// calls; calls that overlap on one device share the array and race.
+static __device__ __align__(256) uint8_t scratch[kPermuteScratchBytes];
+
+namespace {
+constexpr int kMaxScratchDevices = 64;
+std::once_flag g_scratch_once[kMaxScratchDevices];
+void* g_scratch_ptr[kMaxScratchDevices];
+hipError_t g_scratch_err[kMaxScratchDevices];
+}  // namespace
+
+hipError_t permute_scratch(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* p = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = p;
+  });
+  if (g_scratch_err[dev] != hipSuccess) return g_scratch_err[dev];
+  if (g_scratch_ptr[dev] == nullptr) return hipErrorInvalidSymbol;
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_permute_quantize(const int32_t* ids, int64_t T, int32_t k, int32_t E, int32_t align,

@@ -218,6 +218,26 @@ fgg_status fgg_moe_permute_quantize(const int32_t* topk_ids, int64_t T, int32_t 
                                     void* workspace, size_t ws_bytes, void* stream);
 
 /*
+ * fgg_moe_permute_quantize_noalloc — fgg_moe_permute_quantize for callers that
+ * cannot allocate device memory (code under HIP graph capture, serving loops
+ * that forbid allocation): the same arguments without the workspace, the same
+ * outputs bit for bit, and no allocation by the library either.  The per-block
+ * expert histograms live in a static device array of the library (2 MiB per
+ * device, held until the process ends), so the call supports
+ * ceil(T·k / 256) · E <= 524224 (T·k up to 4 193 792 pairs for E = 32, or
+ * 130 816 for E = 1024) and returns FGG_ERR_UNSUPPORTED beyond that, before
+ * launching anything.  Every call on a device uses that device's one array:
+ * calls that overlap on one device (concurrent streams, or host threads
+ * without ordering) race and must be serialized by the caller.  Nothing in the
+ * array needs clearing between calls (every entry is written before it is read).
+ */
+fgg_status fgg_moe_permute_quantize_noalloc(const int32_t* topk_ids, int64_t T, int32_t k, int32_t E, int32_t align,
+                                            const void* x, fgg_dtype x_dtype, int64_t K, int64_t ldx,
+                                            int32_t* offsets, int32_t* counts, int32_t* src_to_row,
+                                            int32_t* row_to_src, void* a_out, float* sa_out, int64_t M_cap,
+                                            void* stream);
+
+/*
  * fgg_grouped_gemm_scaled — one launch for all groups (experts).
  *
  * The per-group formula of [Infra] Q "量化矩阵乘的维度和流程" with both
