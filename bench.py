@@ -302,6 +302,32 @@ def bench_w4a4(fgg, synth, torch, iters=30):
                 value=round(tf, 1), unit="TFLOP/s", mfu_fp4_pct=round(100 * tf / PEAK_FP4_TFLOPS, 2))
 
 
+def bench_mxfp4(fgg, synth, torch, iters=30):
+    """The W4A4 shape in the MX form (E2M1 with E8M0 per 32 on both operands), the
+    same rank-32 branch and bias; the prepared operands are resident, the timed
+    call is the low-rank product plus the GEMM."""
+    M, N, K, r = 4096, 3072, 3072, 32
+    x = synth.normal_cuda(61_000, (M, K)).to(torch.bfloat16)
+    xq, xe = fgg.quantize_blockwise(x, fgg.Q_E2M1_E8M0_1x32)
+    wq, we = fgg.quantize_blockwise(synth.normal_cuda(61_001, (N, K), 0.02), fgg.Q_E2M1_E8M0_1x32)
+    ld = synth.normal_cuda(61_002, (K, r), 0.01).to(torch.bfloat16)
+    lu = synth.normal_cuda(61_003, (r, N), 0.01).to(torch.bfloat16)
+    bias = synth.normal_cuda(61_004, (N,), 0.1).to(torch.bfloat16)
+    d = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(fgg.scaled_gemm_workspace_bytes(M, N, K, "mxfp4", rank=r), dtype=torch.uint8, device="cuda")
+    ms = time_calls(lambda i: fgg.scaled_gemm(xq, xe, wq, we, qdesc="mxfp4", x_bf16=x, l_down=ld, l_up=lu,
+                                              bias=bias, out=d, workspace=ws), iters, 5)
+    flops = 2.0 * M * N * K + 2.0 * M * r * (K + N)
+    tf = flops / (ms * 1e-3) / 1e12
+    nbytes = (M + N) * K // 2 + (M + N) * K // 32 + M * K * 2 + M * N * 2
+    return dict(workload="mxfp4 w4a4 4096x3072x3072 E2M1 + E8M0/32 both operands + rank-32 + bias",
+                us_per_call=round(ms * 1e3, 2), value=round(tf, 1), unit="TFLOP/s",
+                mfu_fp4_pct=round(100 * tf / PEAK_FP4_TFLOPS, 2),
+                roofline=roofline_entry("gemm_mxfp4_kernel (+ low-rank prep launch)", flops, nbytes, ms * 1e-3,
+                                        PEAK_FP4_TFLOPS, "2MNK + 2Mr(K+N) FLOP; bytes = FP4 codes + E8M0 scales "
+                                        "of both operands, the bf16 input of the low-rank branch, bf16 output"))
+
+
 # ----------------------------------------------------------- CPU baseline
 
 def cpu_baseline(synth, target_s=15.0):
@@ -480,6 +506,9 @@ def main():
             "dense": bench_dense(fgg, synth, torch),
             "w4a4": bench_w4a4(fgg, synth, torch),
         }
+        mx = bench_mxfp4(fgg, synth, torch)
+        result["rooflines"]["mxfp4"] = mx.pop("roofline")
+        result["secondary"]["mxfp4"] = mx
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(synth, args.cpu_seconds)
     print(json.dumps(result), flush=True)

@@ -359,9 +359,14 @@ def pack_fp4_weights(b, b_scales, out=None, scales_out=None):
     return out, scales_out
 
 
+def _scaled_qdescs(qdesc):
+    return {"fp8": (Q_E4M3_1x128, Q_E4M3_128x128), "w4a4": (Q_E2M1_1x16, Q_E2M1_1x16),
+            "mxfp4": (Q_E2M1_E8M0_1x32, Q_E2M1_E8M0_1x32)}[qdesc]
+
+
 def scaled_gemm_workspace_bytes(M: int, N: int, K: int, qdesc: str = "fp8", rank: int = 0) -> int:
     """Workspace bytes scaled_gemm needs (fgg_scaled_gemm_workspace)."""
-    aq, bq = (Q_E4M3_1x128, Q_E4M3_128x128) if qdesc == "fp8" else (Q_E2M1_1x16, Q_E2M1_1x16)
+    aq, bq = _scaled_qdescs(qdesc)
     epi = Epilogue(None, None, None, int(rank), None)
     n = ctypes.c_size_t(0)
     _check("fgg_scaled_gemm_workspace", load_library().fgg_scaled_gemm_workspace(
@@ -373,17 +378,14 @@ def scaled_gemm(a, a_scales, b, b_scales, qdesc="fp8", x_bf16=None, l_down=None,
                 out=None, workspace=None):
     """Dense case.  qdesc "fp8": a [M, K] e4m3 with [K/128, M] scales, b [N, K]
     with [N/128, K/128] scales.  qdesc "w4a4": a [M, K/2], b [N, K/2] packed
-    E2M1 with [rows, K/16] fp32 scales, optional low-rank (x_bf16 [M, K],
-    l_down [K, r], l_up [r, N], r = 32) and bias [N] (bf16)."""
+    E2M1 with [rows, K/16] fp32 scales; qdesc "mxfp4": the same codes with
+    [rows, K/32] E8M0 scale bytes.  Both FP4 forms take an optional low-rank
+    branch (x_bf16 [M, K], l_down [K, r], l_up [r, N], r = 32) and bias [N] (bf16)."""
     dev = a.device
     M = a.shape[0]
     N = b.shape[0]
-    if qdesc == "fp8":
-        K = a.shape[1]
-        aq, bq = Q_E4M3_1x128, Q_E4M3_128x128
-    else:
-        K = a.shape[1] * 2
-        aq, bq = Q_E2M1_1x16, Q_E2M1_1x16
+    aq, bq = _scaled_qdescs(qdesc)
+    K = a.shape[1] if qdesc == "fp8" else a.shape[1] * 2
     if out is None:
         out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     epi = None

@@ -13,7 +13,7 @@ CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libfgg.so")
-SOURCES = ["api.hip", "quantize.hip", "permute.hip", "gemm_fp8.hip", "gemm_masked.hip", "gemm_w4a4.hip"]
+SOURCES = ["api.hip", "quantize.hip", "permute.hip", "gemm_fp8.hip", "gemm_masked.hip", "gemm_w4a4.hip", "gemm_mxfp4.hip"]
 ARCH = "gfx950"
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",

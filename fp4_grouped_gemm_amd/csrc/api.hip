@@ -89,7 +89,7 @@ int kernel_table(const KernelInfo* const** out) {
       &kInfoPermuteQuantize, &kInfoFill,              &kInfoCombine,        &kInfoFp8Contig,
       &kInfoFp8ContigSilu,   &kInfoFp8Dense,          &kInfoMaskedFp4Tiled, &kInfoMaskedFp4,
       &kInfoMaskedFp8,       &kInfoPackFp4,           &kInfoPackFp4Scales,  &kInfoW4a4Prep,
-      &kInfoW4a4Gemm,
+      &kInfoW4a4Gemm,        &kInfoMxfp4Gemm,
   };
   *out = table;
   return (int)(sizeof table / sizeof table[0]);
@@ -287,6 +287,8 @@ fgg_status fgg_scaled_gemm_workspace(int64_t M, int64_t N, int64_t K, fgg_qdesc 
   *bytes = 0;
   if (same_q(aq, FGG_E2M1X2, FGG_F32, 1, 16) && same_q(bq, FGG_E2M1X2, FGG_F32, 1, 16))
     *bytes = fgg::w4a4_workspace_bytes(M, N, K, epi ? epi->rank : 0);
+  if (same_q(aq, FGG_E2M1X2, FGG_E8M0, 1, 32) && same_q(bq, FGG_E2M1X2, FGG_E8M0, 1, 32))
+    *bytes = fgg::mxfp4_workspace_bytes(M, epi ? epi->rank : 0);
   return FGG_OK;
 }
 
@@ -294,7 +296,8 @@ fgg_status fgg_scaled_gemm(int64_t M, int64_t N, int64_t K, const void* a, const
                            const void* b, const void* b_scales, fgg_qdesc bq, const fgg_epilogue* epi, void* d,
                            int64_t ldd, void* workspace, size_t ws_bytes, void* stream) {
   if (M < 0 || N < 0 || K < 0) return FGG_ERR_INVALID_VALUE;
-  if (N % 128 != 0 || K % 128 != 0) return FGG_ERR_UNSUPPORTED;
+  // (N % 128 for the FP8 and per-16 W4A4 paths, N % 16 for MXFP4: checked per path below)
+  if (N % 16 != 0 || K % 128 != 0) return FGG_ERR_UNSUPPORTED;
   if (ldd < N || ldd % 8 != 0) return FGG_ERR_INVALID_VALUE;
   // (with K == 0 the operands hold no bytes and are never read: they may be NULL)
   if ((K > 0 && (!a || !a_scales || !b || !b_scales)) || !d) return FGG_ERR_INVALID_VALUE;
@@ -302,7 +305,7 @@ fgg_status fgg_scaled_gemm(int64_t M, int64_t N, int64_t K, const void* a, const
     return FGG_ERR_INVALID_VALUE;
   int num_cus = 0;
   if (same_q(aq, FGG_E4M3, FGG_F32, 1, 128) && same_q(bq, FGG_E4M3, FGG_F32, 128, 128)) {
-    if (epi) return FGG_ERR_UNSUPPORTED;
+    if (epi || N % 128 != 0) return FGG_ERR_UNSUPPORTED;
     if (K > 16384) return FGG_ERR_UNSUPPORTED;
     fgg_status st = device_check(&num_cus);
     if (st != FGG_OK) return st;
@@ -313,7 +316,7 @@ fgg_status fgg_scaled_gemm(int64_t M, int64_t N, int64_t K, const void* a, const
   }
   if (same_q(aq, FGG_E2M1X2, FGG_F32, 1, 16) && same_q(bq, FGG_E2M1X2, FGG_F32, 1, 16)) {
     // (the GEMM's per-lane DMA offsets are 32-bit: 128 rows x 2K bytes)
-    if (M % 128 != 0 || K == 0 || K > (int64_t(1) << 22)) return FGG_ERR_UNSUPPORTED;
+    if (M % 128 != 0 || N % 128 != 0 || K == 0 || K > (int64_t(1) << 22)) return FGG_ERR_UNSUPPORTED;
     if (!aligned(a_scales, 8) || !aligned(b_scales, 8)) return FGG_ERR_INVALID_VALUE;
     const int32_t rank = epi ? epi->rank : 0;
     if (rank != 0 && rank != 32) return FGG_ERR_UNSUPPORTED;
@@ -335,6 +338,30 @@ fgg_status fgg_scaled_gemm(int64_t M, int64_t N, int64_t K, const void* a, const
                                    rank ? (const uint16_t*)epi->l_down : nullptr,
                                    rank ? (const uint16_t*)epi->l_up : nullptr, rank, (const uint16_t*)bias,
                                    (uint16_t*)d, ldd, workspace, num_cus, (hipStream_t)stream));
+  }
+  if (same_q(aq, FGG_E2M1X2, FGG_E8M0, 1, 32) && same_q(bq, FGG_E2M1X2, FGG_E8M0, 1, 32)) {
+    // (per-lane DMA offsets are 32-bit: 256 rows x K/2 bytes)
+    if (K == 0 || K > (int64_t(1) << 24)) return FGG_ERR_UNSUPPORTED;
+    // (scale rows are read as dwords: K/32 bytes per row, a multiple of 4)
+    const int32_t rank = epi ? epi->rank : 0;
+    if (rank != 0 && rank != 32) return FGG_ERR_UNSUPPORTED;
+    if (rank == 32) {
+      if (!epi->x_bf16 || !epi->l_down || !epi->l_up) return FGG_ERR_INVALID_VALUE;
+      if (!aligned(epi->x_bf16, 16) || !aligned(epi->l_down, 2) || !aligned(epi->l_up, 2))
+        return FGG_ERR_INVALID_VALUE;
+      if (M > 0 && N > 0 && (!workspace || ws_bytes < fgg::mxfp4_workspace_bytes(M, rank) || !aligned(workspace, 16)))
+        return FGG_ERR_INVALID_VALUE;
+    }
+    const void* bias = epi ? epi->bias : nullptr;
+    if (bias && !aligned(bias, 2)) return FGG_ERR_INVALID_VALUE;
+    fgg_status st = device_check(&num_cus);
+    if (st != FGG_OK) return st;
+    if (M == 0 || N == 0) return FGG_OK;
+    return finish(fgg::launch_mxfp4(M, N, K, (const uint8_t*)a, (const uint8_t*)a_scales, (const uint8_t*)b,
+                                    (const uint8_t*)b_scales, rank ? (const uint16_t*)epi->x_bf16 : nullptr,
+                                    rank ? (const uint16_t*)epi->l_down : nullptr,
+                                    rank ? (const uint16_t*)epi->l_up : nullptr, rank, (const uint16_t*)bias,
+                                    (uint16_t*)d, ldd, workspace, (hipStream_t)stream));
   }
   return FGG_ERR_UNSUPPORTED;
 }

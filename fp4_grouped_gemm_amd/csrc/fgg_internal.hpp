@@ -37,7 +37,7 @@ extern const KernelInfo kInfoQuantE4m3_1x128, kInfoQuantE4m3_128x128, kInfoQuant
     kInfoQuantE2m1E8m0_1x32, kInfoPermuteHist, kInfoPermuteScan, kInfoPermuteScatter, kInfoPermuteGather,
     kInfoPermuteQuantize, kInfoFill, kInfoCombine, kInfoFp8Contig, kInfoFp8ContigSilu, kInfoFp8Dense,
     kInfoMaskedFp4Tiled, kInfoMaskedFp4, kInfoMaskedFp8, kInfoPackFp4, kInfoPackFp4Scales, kInfoW4a4Prep,
-    kInfoW4a4Gemm;
+    kInfoW4a4Gemm, kInfoMxfp4Gemm;
 
 enum class QuantKind { E4M3_1x128, E4M3_128x128, E2M1_1x16, E2M1_E8M0_1x32 };
 
@@ -98,5 +98,16 @@ hipError_t launch_w4a4(int64_t M, int64_t N, int64_t K, const uint8_t* a, const 
                        const uint8_t* b, const float* sb, const uint16_t* x_bf16,
                        const uint16_t* l_down, const uint16_t* l_up, int32_t rank,
                        const uint16_t* bias, uint16_t* d, int64_t ldd, void* ws, int num_cus, hipStream_t st);
+
+// T = bf16(X · L_down), rank 32 ([M][32]), by the low-rank blocks of the W4A4 preparation kernel.
+hipError_t launch_lowrank_t(int64_t M, int64_t K, const uint16_t* x_bf16, const uint16_t* l_down, uint16_t* T,
+                            hipStream_t st);
+
+// MXFP4 A4W4: E2M1 with E8M0 per 32 on both operands (scales [rows][K/32] bytes), optional
+// rank-32 low-rank branch (workspace: T [M][32] bf16) and bias.
+size_t mxfp4_workspace_bytes(int64_t M, int32_t rank);
+hipError_t launch_mxfp4(int64_t M, int64_t N, int64_t K, const uint8_t* a, const uint8_t* sa, const uint8_t* b,
+                        const uint8_t* sb, const uint16_t* x_bf16, const uint16_t* l_down, const uint16_t* l_up,
+                        int32_t rank, const uint16_t* bias, uint16_t* d, int64_t ldd, void* ws, hipStream_t st);
 
 }  // namespace fgg

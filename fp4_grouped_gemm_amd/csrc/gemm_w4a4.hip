@@ -368,6 +368,17 @@ size_t w4a4_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t rank) {
   return b;
 }
 
+hipError_t launch_lowrank_t(int64_t M, int64_t K, const uint16_t* x_bf16, const uint16_t* l_down, uint16_t* T,
+                            hipStream_t st) {
+  // only the low-rank blocks of the preparation kernel (no operand to dequantize)
+  const int64_t lr_blocks = (M + 15) / 16;
+  trace_launch(kInfoW4a4Prep, dim3((unsigned)lr_blocks), "M=%lld K=%lld rank=32 (low-rank blocks only)", (long long)M,
+               (long long)K);
+  hipLaunchKernelGGL(w4a4_prep_kernel, dim3((unsigned)lr_blocks), dim3(256), 0, st, nullptr, nullptr, (int64_t)0,
+                     nullptr, nullptr, nullptr, (int64_t)0, nullptr, x_bf16, l_down, T, M, K, lr_blocks);
+  return hipGetLastError();
+}
+
 const KernelInfo kInfoW4a4Prep = {"w4a4_prep_kernel", "fgg_scaled_gemm (W4A4)", 16, 32, 0, 256, 0, 0,
                                   kLrWaves * 32 * 32 * 2 + kLrWaves * 2 * 64 * 16,
                                   kLrWaves * 32 * 32 * 2 + kLrWaves * 2 * 64 * 16, (const void*)w4a4_prep_kernel};

@@ -355,7 +355,17 @@ fgg_status fgg_pack_fp4_weights(const void* b, const void* b_scales, int32_t G, 
  *   |code · s| <= 6·s must fit: a 16-element group whose largest magnitude is
  *   at or above 65520 (s >= 10920) would become inf, and values below 2^-24
  *   flush to zero.  The call checks nothing of this on the device (it would
- *   need a pass over the scales).
+ *   need a pass over the scales); callers whose activations can leave the fp16
+ *   range use the MXFP4 form below, whose E8M0 scales span 2^-127..2^127.
+ * aq = bq = {E2M1X2,E8M0,1,32} (MXFP4 W4A4): a [M][K/2], a_scales [M][K/32]
+ *   E8M0 bytes; b [N][K/2], b_scales [N][K/32]; the same epilogue:
+ *   D = bf16( Σ_g32 2^(ea[m,g]-127)·2^(eb[n,g]-127)·Σ_{k in g} A[m][k]·B[n][k]
+ *             + (x_bf16 · l_down) · l_up + bias )
+ *   The E8M0 scales are applied by the FP4 matrix instruction itself (no
+ *   dequantization, no promotion), fp32 accumulation; the rank-32 intermediate
+ *   x_bf16 · l_down is rounded to bf16 as above.  Any M >= 0, N % 16 == 0,
+ *   K % 128 == 0, 128 <= K <= 2^24, rank in {0, 32}; workspace (16-byte
+ *   aligned) holds the [M][32] intermediate when rank is 32, else none.
  *   Requires M % 128 == 0, K % 128 == 0, 128 <= K <= 2^22, N % 128 == 0, rank in {0, 32}.
  *   workspace (256-byte aligned) must hold fgg_scaled_gemm_workspace() bytes:
  *   the fp16 copies of A and B, and with a low-rank branch the [M][32]

@@ -120,6 +120,22 @@ def test_gemm_and_permute_reject_bad_arguments_on_host():
     assert lib.fgg_scaled_gemm(256, 128, 256, g, g, W, g, g, W, None, g, 128, None, 0, None) == 1
     # W4A4 with K == 0 is not supported
     assert lib.fgg_scaled_gemm(256, 128, 0, g, g, W, g, g, W, None, g, 128, None, 0, None) == 2
+    # N % 128 for the FP8 and per-16 W4A4 forms; MXFP4 takes N % 16 but not N % 8
+    F8a, F8b = _q(fgg.Q_E4M3_1x128), _q(fgg.Q_E4M3_128x128)
+    assert lib.fgg_scaled_gemm(256, 192, 256, g, g, F8a, g, g, F8b, None, g, 192, None, 0, None) == 2
+    assert lib.fgg_scaled_gemm(256, 192, 256, g, g, W, g, g, W, None, g, 192, g, 1 << 22, None) == 2
+    MX = _q(fgg.Q_E2M1_E8M0_1x32)
+    assert lib.fgg_scaled_gemm(256, 200, 256, g, g, MX, g, g, MX, None, g, 200, None, 0, None) == 2
+    assert lib.fgg_scaled_gemm(256, 192, 0, g, g, MX, g, g, MX, None, g, 192, None, 0, None) == 2
+    # MXFP4: rank 16 is not supported; rank 32 needs its [M][32] workspace
+    epi16 = fgg.Epilogue(4096, 4096, 4096, 16, None)
+    assert lib.fgg_scaled_gemm(256, 192, 256, g, g, MX, g, g, MX, ctypes.byref(epi16), g, 192, g, 1 << 20, None) == 2
+    epi32 = fgg.Epilogue(4096, 4096, 4096, 32, None)
+    assert lib.fgg_scaled_gemm_workspace(256, 192, 256, MX, MX, ctypes.byref(epi32), ctypes.byref(nbytes)) == 0
+    assert nbytes.value == 256 * 32 * 2
+    assert lib.fgg_scaled_gemm(256, 192, 256, g, g, MX, g, g, MX, ctypes.byref(epi32), g, 192, g, 100, None) == 1
+    assert lib.fgg_scaled_gemm_workspace(256, 192, 256, MX, MX, None, ctypes.byref(nbytes)) == 0
+    assert nbytes.value == 0
     # permute: bad k / E, missing workspace
     assert lib.fgg_moe_permute(g, 10, 0, 4, 128, None, None, 0, g, g, g, g, None, None, 100, g, 1 << 20, None) == 1
     assert lib.fgg_moe_permute(g, 10, 2, 2000, 128, None, None, 0, g, g, g, g, None, None, 100, g, 1 << 20, None) == 1
