@@ -20,6 +20,9 @@ FLAGS = [
     "-munsafe-fp-atomics",
     # keep the compiler from forming packed fp32 VALU ops (not trusted on this part)
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # only the C ABI is exported (api.hip marks it); internal functions and kernel stubs stay
+    # local, so two builds loaded in one process (a same-process A/B) each run their own code
+    "-fvisibility=hidden", "-fvisibility-inlines-hidden",
     "-I", os.path.join(ROOT, "include"),
 ]
 
@@ -48,7 +51,7 @@ def build(verbose: bool = True) -> str:
     with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = LIB + ".tmp"
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Wl,-Bsymbolic", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stdout + r.stderr)

@@ -97,6 +97,8 @@ int kernel_table(const KernelInfo* const** out) {
 
 }  // namespace fgg
 
+// The C ABI is the library's only export (the build hides everything else).
+#pragma GCC visibility push(default)
 extern "C" {
 
 const char* fgg_status_string(fgg_status s) {
@@ -439,3 +441,4 @@ fgg_status fgg_kernel_compiled_lds(int32_t i, int64_t* bytes) {
 }
 
 }  // extern "C"
+#pragma GCC visibility pop
