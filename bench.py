@@ -302,6 +302,42 @@ def bench_w4a4(fgg, synth, torch, iters=30):
                 value=round(tf, 1), unit="TFLOP/s", mfu_fp4_pct=round(100 * tf / PEAK_FP4_TFLOPS, 2))
 
 
+def bench_down_combine(fgg, st, torch, iters=30):
+    """The prefill step's down projection + combine as one call (fgg_moe_down_combine)
+    against the two calls it replaces, on the step's own data (alternating, medians)."""
+    import numpy as np
+    b, p = st["bufs"], st["perm"]
+    ws = torch.empty(fgg.moe_down_combine_workspace_bytes(b["a2"].shape[0]), dtype=torch.uint8, device="cuda")
+    y2, out2 = torch.empty_like(b["y"]), torch.empty_like(b["out"])
+
+    def two():
+        fgg.grouped_gemm_scaled(b["a2"], b["s2"], st["dn_q"], st["dn_s"], offsets=p["offsets"],
+                                masked_m=p["counts"], out=b["y"])
+        fgg.moe_combine(b["y"], p["src_to_row"], st["tw"], out=b["out"])
+
+    def fused():
+        fgg.moe_down_combine(b["a2"], b["s2"], st["dn_q"], st["dn_s"], p["offsets"], p["counts"], p["src_to_row"],
+                             p["row_to_src"], st["tw"], y2, out=out2, workspace=ws)
+
+    two()
+    fused()
+    _sync()
+    same = bool(torch.equal(b["out"].view(torch.int16), out2.view(torch.int16)))
+    t = ([], [])
+    for i in range(2 * iters + 4):
+        fn = (two, fused)[i % 2]
+        a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        z.record()
+        _sync()
+        if i >= 4:
+            t[i % 2].append(a.elapsed_time(z) * 1e3)
+    return {"workload": "prefill down GEMM (N=7168, K=2048, counts) + combine (T=8192, k=8)",
+            "two_calls_us": round(float(np.median(t[0])), 2), "fused_us": round(float(np.median(t[1])), 2),
+            "bit_identical": same}
+
+
 def bench_mxfp4(fgg, synth, torch, iters=30):
     """The W4A4 shape in the MX form (E2M1 with E8M0 per 32 on both operands), the
     same rank-32 branch and bias; the prepared operands are resident, the timed
@@ -506,6 +542,7 @@ def main():
             "dense": bench_dense(fgg, synth, torch),
             "w4a4": bench_w4a4(fgg, synth, torch),
         }
+        result["secondary"]["moe_down_combine"] = bench_down_combine(fgg, st, torch)
         mx = bench_mxfp4(fgg, synth, torch)
         result["rooflines"]["mxfp4"] = mx.pop("roofline")
         result["secondary"]["mxfp4"] = mx

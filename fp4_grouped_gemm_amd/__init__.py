@@ -93,6 +93,9 @@ def load_library():
         "fgg_scaled_gemm_workspace": ([I64, I64, I64, QDesc, QDesc, ctypes.POINTER(Epilogue), ctypes.POINTER(SZ)], I32),
         "fgg_scaled_gemm": ([I64, I64, I64, P, P, QDesc, P, P, QDesc, ctypes.POINTER(Epilogue), P, I64, P, SZ, P], I32),
         "fgg_moe_combine": ([P, I64, P, P, I64, I32, I64, P, I64, P], I32),
+        "fgg_moe_down_combine_workspace": ([I64, ctypes.POINTER(SZ)], I32),
+        "fgg_moe_down_combine": ([I32, I64, I64, I64, P, P, QDesc, P, P, QDesc, P, P, P, P, P, I64, I32, P, I64, P, SZ,
+                                  P, I64, P], I32),
         "fgg_pack_fp4_weights_bytes": ([I32, I64, I64, ctypes.POINTER(SZ), ctypes.POINTER(SZ)], I32),
         "fgg_pack_fp4_weights": ([P, P, I32, I64, I64, P, P, P], I32),
     }
@@ -418,4 +421,34 @@ def moe_combine(y, src_to_row, topk_w, out=None):
     st = load_library().fgg_moe_combine(_ptr(y), y.stride(0), _ptr(src_to_row), _ptr(topk_w), T, k, N,
                                          _ptr(out), out.stride(0), _stream(dev))
     _check("fgg_moe_combine", st)
+    return out
+
+
+def moe_down_combine_workspace_bytes(M: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check("fgg_moe_down_combine_workspace", load_library().fgg_moe_down_combine_workspace(M, ctypes.byref(n)))
+    return n.value
+
+
+def moe_down_combine(a, a_scales, b, b_scales, offsets, counts, src_to_row, row_to_src, topk_w, y, out=None,
+                     workspace=None):
+    """Down GEMM and combine in one call (fgg_moe_down_combine): ``out`` equals
+    ``moe_combine(grouped_gemm_scaled(a, ..., offsets, masked_m=counts), src_to_row, topk_w)``
+    bit for bit.  ``y`` (bf16 [M, N]) receives the rows of tokens with two or more
+    routed slots; rows of single-slot tokens go straight to ``out`` (bf16 [T, N])."""
+    G, N, K = b.shape
+    M = a.shape[0]
+    T, k = topk_w.shape
+    dev = a.device
+    for t in (a, a_scales, b, b_scales, offsets, counts, src_to_row, row_to_src, topk_w):
+        assert t.is_contiguous()
+    if out is None:
+        out = torch.empty((T, N), dtype=torch.bfloat16, device=dev)
+    if workspace is None:
+        workspace = torch.empty(moe_down_combine_workspace_bytes(M), dtype=torch.uint8, device=dev)
+    st = load_library().fgg_moe_down_combine(
+        G, M, N, K, _ptr(a), _ptr(a_scales), _q(Q_E4M3_1x128), _ptr(b), _ptr(b_scales), _q(Q_E4M3_128x128),
+        _ptr(offsets), _ptr(counts), _ptr(src_to_row), _ptr(row_to_src), _ptr(topk_w), T, k, _ptr(y), y.stride(0),
+        _ptr(workspace), workspace.numel(), _ptr(out), out.stride(0), _stream(dev))
+    _check("fgg_moe_down_combine", st)
     return out

@@ -86,8 +86,9 @@ int kernel_table(const KernelInfo* const** out) {
   static const KernelInfo* const table[] = {
       &kInfoQuantE4m3_1x128, &kInfoQuantE4m3_128x128, &kInfoQuantE2m1_1x16, &kInfoQuantE2m1E8m0_1x32,
       &kInfoPermuteHist,     &kInfoPermuteScan,       &kInfoPermuteScatter, &kInfoPermuteGather,
-      &kInfoPermuteQuantize, &kInfoFill,              &kInfoCombine,        &kInfoFp8Contig,
-      &kInfoFp8ContigSilu,   &kInfoFp8Dense,          &kInfoMaskedFp4Tiled, &kInfoMaskedFp4,
+      &kInfoPermuteQuantize, &kInfoFill,              &kInfoCombine,        &kInfoCombineRows,
+      &kInfoCombineRest,     &kInfoFp8Contig,         &kInfoFp8ContigSilu,  &kInfoFp8ContigCombine,
+      &kInfoFp8Dense,        &kInfoMaskedFp4Tiled,    &kInfoMaskedFp4,
       &kInfoMaskedFp8,       &kInfoPackFp4,           &kInfoPackFp4Scales,  &kInfoW4a4Prep,
       &kInfoW4a4Gemm,        &kInfoMxfp4Gemm,
   };
@@ -402,6 +403,46 @@ fgg_status fgg_moe_combine(const void* y, int64_t ldy, const int32_t* src_to_row
   if (st != FGG_OK) return st;
   return finish(fgg::launch_combine((const uint16_t*)y, ldy, src_to_row, topk_w, T, k, N, (uint16_t*)out, ldo,
                                     (hipStream_t)stream));
+}
+
+fgg_status fgg_moe_down_combine_workspace(int64_t M, size_t* bytes) {
+  if (!bytes || M < 0) return FGG_ERR_INVALID_VALUE;
+  *bytes = (size_t)((M + 127) / 128 * 128) * 8;
+  return FGG_OK;
+}
+
+fgg_status fgg_moe_down_combine(int32_t G, int64_t M, int64_t N, int64_t K, const void* a, const void* a_scales,
+                                fgg_qdesc aq, const void* b, const void* b_scales, fgg_qdesc bq,
+                                const int32_t* offsets, const int32_t* counts, const int32_t* src_to_row,
+                                const int32_t* row_to_src, const float* topk_w, int64_t T, int32_t k, void* y,
+                                int64_t ldy, void* workspace, size_t ws_bytes, void* out, int64_t ldo,
+                                void* stream) {
+  if (G < 1 || G > 1024 || M < 0 || N < 0 || K < 0 || T < 0 || k < 1 || k > 64) return FGG_ERR_INVALID_VALUE;
+  if (N % 128 != 0 || K % 128 != 0 || K > 16384) return FGG_ERR_UNSUPPORTED;
+  if (!same_q(aq, FGG_E4M3, FGG_F32, 1, 128) || !same_q(bq, FGG_E4M3, FGG_F32, 128, 128)) return FGG_ERR_UNSUPPORTED;
+  if (ldy < N || ldy % 8 != 0 || ldo < N || ldo % 8 != 0) return FGG_ERR_INVALID_VALUE;
+  if ((K > 0 && (!a || !a_scales || !b || !b_scales)) || !offsets || !counts || !src_to_row || !row_to_src ||
+      !topk_w || !y || !out)
+    return FGG_ERR_INVALID_VALUE;
+  if (!aligned(a, 16) || !aligned(b, 16) || !aligned(y, 16) || !aligned(out, 16) || !aligned(a_scales, 4) ||
+      !aligned(b_scales, 4) || !aligned(topk_w, 4))
+    return FGG_ERR_INVALID_VALUE;
+  size_t need = 0;
+  fgg_moe_down_combine_workspace(M, &need);
+  if (M > 0 && (!workspace || !aligned(workspace, 16) || ws_bytes < need)) return FGG_ERR_INVALID_VALUE;
+  int num_cus = 0;
+  fgg_status st = device_check(&num_cus);
+  if (st != FGG_OK) return st;
+  const hipStream_t hs = (hipStream_t)stream;
+  uint8_t* ri = (uint8_t*)workspace;
+  hipError_t e = fgg::launch_combine_rows(row_to_src, src_to_row, topk_w, T, k, M, ri, hs);
+  if (e == hipSuccess)
+    e = fgg::launch_gemm_fp8_combine(G, M, N, K, (const uint8_t*)a, (const float*)a_scales, (const uint8_t*)b,
+                                     (const float*)b_scales, offsets, counts, (uint16_t*)y, ldy, ri, (uint16_t*)out,
+                                     ldo, num_cus, hs);
+  if (e == hipSuccess)
+    e = fgg::launch_combine_rest((const uint16_t*)y, ldy, src_to_row, topk_w, T, k, N, (uint16_t*)out, ldo, hs);
+  return finish(e);
 }
 
 int32_t fgg_kernel_count(void) {

@@ -35,7 +35,8 @@ void trace_launch(const KernelInfo& k, dim3 grid, const char* fmt, ...) __attrib
 
 extern const KernelInfo kInfoQuantE4m3_1x128, kInfoQuantE4m3_128x128, kInfoQuantE2m1_1x16,
     kInfoQuantE2m1E8m0_1x32, kInfoPermuteHist, kInfoPermuteScan, kInfoPermuteScatter, kInfoPermuteGather,
-    kInfoPermuteQuantize, kInfoFill, kInfoCombine, kInfoFp8Contig, kInfoFp8ContigSilu, kInfoFp8Dense,
+    kInfoPermuteQuantize, kInfoFill, kInfoCombine, kInfoCombineRows, kInfoCombineRest, kInfoFp8Contig,
+    kInfoFp8ContigSilu, kInfoFp8ContigCombine, kInfoFp8Dense,
     kInfoMaskedFp4Tiled, kInfoMaskedFp4, kInfoMaskedFp8, kInfoPackFp4, kInfoPackFp4Scales, kInfoW4a4Prep,
     kInfoW4a4Gemm, kInfoMxfp4Gemm;
 
@@ -66,6 +67,17 @@ hipError_t launch_permute_quantize(const int32_t* ids, int64_t T, int32_t k, int
 hipError_t launch_combine(const uint16_t* y, int64_t ldy, const int32_t* src_to_row, const float* w,
                           int64_t T, int32_t k, int64_t N, uint16_t* out, int64_t ldo,
                           hipStream_t st);
+// The down GEMM with the combine of single-slot tokens in its epilogue: the routing
+// table (row_info, roundup(M, 128) entries of 8 bytes: token or -1, weight), the GEMM,
+// then the combine of the other tokens.
+hipError_t launch_combine_rows(const int32_t* row_to_src, const int32_t* src_to_row, const float* w, int64_t T,
+                               int32_t k, int64_t M, uint8_t* row_info, hipStream_t st);
+hipError_t launch_gemm_fp8_combine(int32_t G, int64_t M, int64_t N, int64_t K, const uint8_t* a, const float* sa,
+                                   const uint8_t* b, const float* sb, const int32_t* offsets, const int32_t* valid,
+                                   uint16_t* y, int64_t ldy, const uint8_t* row_info, uint16_t* out, int64_t ldo,
+                                   int num_cus, hipStream_t st);
+hipError_t launch_combine_rest(const uint16_t* y, int64_t ldy, const int32_t* src_to_row, const float* w, int64_t T,
+                               int32_t k, int64_t N, uint16_t* out, int64_t ldo, hipStream_t st);
 
 // FP8 x FP8 grouped GEMM, contiguous layout (dense = one group with offsets {0, M}).
 // If offsets == nullptr the single group covers rows [0, M).  valid (nullable, with

@@ -80,7 +80,9 @@ constexpr int kSBStage = 16;
 constexpr int kMaxG = 1024;
 // per workgroup: offsets[0..G] and each group's end of real rows (offsets[g] + count)
 constexpr int kGrpOff = kSBOff + kStages * kSBStage;
-// SILU epilogue: per-row partial maxima of the 4 column waves, [2 row halves][4][64]
+// SILU epilogue: per-row partial maxima of the 4 column waves, [2 row halves][4][64];
+// COMBINE epilogue (the plain instance): the tile's per-row routing table, two 1 KB
+// buffers of 128 (token, weight) pairs, alternating between consecutive tiles
 constexpr int kRedOff = kGrpOff + (2 * kMaxG + 1) * 4;
 constexpr int kLdsBytes = kRedOff + 2 * 4 * 64 * 4;
 constexpr int kADma = kABytes / 1024 / kWaves;   // 16-byte-per-lane DMA instructions per wave
@@ -168,18 +170,27 @@ __device__ inline int find_group(const int32_t* offs, int G, int64_t row) {
 template <bool SILU>
 __device__ constexpr int bfrag_row(int j) { return SILU ? (j & 1) * 16 + (j >> 1) * 128 : 16 * j; }
 
+// COMBINE (plain instance only): the down GEMM with the gate-weighted combine of
+// single-slot tokens in the epilogue.  RI [rows] holds per permuted row the token it
+// belongs to and its gate weight when that token has exactly one routed slot (else
+// token -1); such a row is written to O[token] as bf16(w · bf16(d)) (the combine's
+// arithmetic for one slot) instead of to D.  The tile's 128 entries (1 KB) travel into
+// LDS with its first stage's DMA.
+//
 // SILU: the gate-up GEMM with SiLU(gate)·up and the 1x128 e4m3 requantization in the
 // epilogue.  B has N = 2I rows ([gate | up]); the tile of output block j (128
 // columns of the activation) takes gate rows [128j, 128j+128) and up rows
 // [I+128j, I+128j+128) as its 256 columns, so each row's gate and up values meet in
 // one workgroup.  Writes Q [rows][I] e4m3 and S [I/128][M] fp32 instead of D.
-template <bool SILU>
+template <bool SILU, bool COMBINE = false>
 __global__ void __launch_bounds__(kThreads, 1)
 gemm_fp8_contig_kernel(int G, int64_t M, int64_t N, int64_t K, const uint8_t* __restrict__ A,
                        const float* __restrict__ SA, const uint8_t* __restrict__ B,
                        const float* __restrict__ SB, const int32_t* __restrict__ offsets,
                        const int32_t* __restrict__ valid, uint16_t* __restrict__ D, int64_t ldd,
-                       uint8_t* __restrict__ Q, float* __restrict__ S) {
+                       uint8_t* __restrict__ Q, float* __restrict__ S, const uint8_t* __restrict__ RI,
+                       uint16_t* __restrict__ O, int64_t ldo) {
+  static_assert(!(SILU && COMBINE), "the combine epilogue belongs to the plain instance");
   __shared__ __align__(16) uint8_t smem[kLdsBytes];
   const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
   const int tid = threadIdx.x;
@@ -317,6 +328,8 @@ gemm_fp8_contig_kernel(int G, int64_t M, int64_t N, int64_t K, const uint8_t* __
   const float* SAt = SA;
   const float* SBg = SB;
   uint32_t offA[kADma], offB[kBDma], offS = 0, offSB = 0;
+  const uint8_t* RIt = RI;
+  int ri_slot = 1;                     // routing-table buffer of the DMA tile (COMBINE)
   auto set_dma = [&](const Tile& t) {
     Atile = uniform_ptr(A + t.m0 * K);
     // this wave's B DMA rows are tile rows [32 * wave, 32 * wave + 32): with SILU, waves
@@ -325,6 +338,10 @@ gemm_fp8_contig_kernel(int G, int64_t M, int64_t N, int64_t K, const uint8_t* __
     Btile = uniform_ptr(B + ((int64_t)t.g * N + b_first) * K);
     SAt = uniform_ptr(SA + t.m0);
     SBg = uniform_ptr(SB + (int64_t)t.g * nblk * nkb);
+    if constexpr (COMBINE) {
+      RIt = uniform_ptr(RI + t.m0 * 8);
+      ri_slot ^= 1;
+    }
     const int lane_t = opaque(lane);
     const int lrow = lane_t >> 3, lchunk = (lane_t & 7) ^ lrow;
 #pragma unroll
@@ -366,6 +383,11 @@ gemm_fp8_contig_kernel(int G, int64_t M, int64_t N, int64_t K, const uint8_t* __
     const float* s_src = SAt + (int64_t)kb * M;
     if (lane < kSRows) dma4(s_src, offS, lds_base + kSOff + stage * kSBytes + wave * kSRows * 4);
     if (wave == 0 && lane < 2) dma4(SBg + kb, offSB, lds_base + kSBOff + stage * kSBStage);
+    // COMBINE: the tile's 128 routing entries with its first stage, by the last wave (one
+    // more instruction in stage 0 only: the waits for later stages are unchanged, and a
+    // tile's first wait is for everything)
+    if constexpr (COMBINE)
+      if (kb == 0 && wave == kWaves - 1) dma16(RIt, (uint32_t)(lane * 16), lds_base + kRedOff + ri_slot * 1024);
   };
 
   // this wave's weight scales: its 64 columns lie in column half (wn * 64) / 128; with
@@ -635,16 +657,37 @@ gemm_fp8_contig_kernel(int G, int64_t M, int64_t N, int64_t K, const uint8_t* __
     if constexpr (!SILU) {
       if (wn * kWaveCols < cur.cols_here && busy) {
         const int lane_e = opaque(lane);
+        const uint2* ri = reinterpret_cast<const uint2*>(smem + kRedOff + ri_slot * 1024);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int r = wm * 64 + 16 * i + (lane_e & 15);
           if (r >= cur.rows_valid) continue;
           const int64_t row = cur.m0 + r;
+          // bf16 of the row's 16 values; with COMBINE, a single-slot token's row goes to its
+          // output row instead, as bf16(w · bf16(d)) with the product formed as the combine
+          // forms it (an fma onto +0, so a -0 product becomes +0); both values are formed
+          // in every lane and the store takes one of them (no divergent branch)
           uint16_t* drow = D + row * ldd + cur.n0 + wn * kWaveCols + 4 * (lane_e >> 4);
+          bool single = false;
+          float w = 0.0f;
+          if constexpr (COMBINE) {
+            const uint2 e = ri[r];
+            single = (int)e.x >= 0;
+            w = __uint_as_float(e.y);
+            if (single) drow = O + (int64_t)(int)e.x * ldo + cur.n0 + wn * kWaveCols + 4 * (lane_e >> 4);
+          }
 #pragma unroll
           for (int j = 0; j < kNFrag; ++j) {
-            const uint32_t lo = (uint32_t)bf16_bits_rne(acc[i][j][0]) | ((uint32_t)bf16_bits_rne(acc[i][j][1]) << 16);
-            const uint32_t hi = (uint32_t)bf16_bits_rne(acc[i][j][2]) | ((uint32_t)bf16_bits_rne(acc[i][j][3]) << 16);
+            uint32_t lo = bf16x2_rne(acc[i][j][0], acc[i][j][1]);
+            uint32_t hi = bf16x2_rne(acc[i][j][2], acc[i][j][3]);
+            if constexpr (COMBINE) {
+              const uint32_t lo_c = bf16x2_rne(fmaf(w, __uint_as_float(lo << 16), 0.0f),
+                                               fmaf(w, __uint_as_float(lo & 0xFFFF0000u), 0.0f));
+              const uint32_t hi_c = bf16x2_rne(fmaf(w, __uint_as_float(hi << 16), 0.0f),
+                                               fmaf(w, __uint_as_float(hi & 0xFFFF0000u), 0.0f));
+              lo = single ? lo_c : lo;
+              hi = single ? hi_c : hi;
+            }
             *reinterpret_cast<uint2*>(drow + 16 * j) = make_uint2(lo, hi);
           }
         }
@@ -865,8 +908,8 @@ gemm_fp8_dense_kernel(int64_t M, int64_t N, int64_t K, const uint8_t* __restrict
       uint16_t* drow = D + row * ldd + n0 + wn * 64 + 4 * q;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const uint32_t lo = (uint32_t)bf16_bits_rne(acc[i][j][0]) | ((uint32_t)bf16_bits_rne(acc[i][j][1]) << 16);
-        const uint32_t hi = (uint32_t)bf16_bits_rne(acc[i][j][2]) | ((uint32_t)bf16_bits_rne(acc[i][j][3]) << 16);
+        const uint32_t lo = bf16x2_rne(acc[i][j][0], acc[i][j][1]);
+        const uint32_t hi = bf16x2_rne(acc[i][j][2], acc[i][j][3]);
         *reinterpret_cast<uint2*>(drow + 16 * j) = make_uint2(lo, hi);
       }
     }
@@ -881,6 +924,10 @@ const KernelInfo kInfoFp8ContigSilu = {
     "gemm_fp8_contig_kernel<silu>", "fgg_grouped_gemm_silu_quantize", BM, BN, BK, kThreads, kStages,
     kABytes + kSBytes + kBBytes + kSBStage, (2 * kMaxG + 1) * 4 + 2 * 4 * 64 * 4, kLdsBytes,
     (const void*)gemm_fp8_contig_kernel<true>};
+const KernelInfo kInfoFp8ContigCombine = {
+    "gemm_fp8_contig_kernel<combine>", "fgg_moe_down_combine", BM, BN, BK, kThreads, kStages,
+    kABytes + kSBytes + kBBytes + kSBStage, (2 * kMaxG + 1) * 4 + 2 * 4 * 64 * 4, kLdsBytes,
+    (const void*)gemm_fp8_contig_kernel<false, true>};
 const KernelInfo kInfoFp8Dense = {"gemm_fp8_dense_kernel", "fgg_scaled_gemm (fp8)", dense::BM, dense::BN, dense::BK,
                                   dense::kThreads, 2, dense::kStageBytes, 2 * dense::kMaxKb * 4, dense::kLdsBytes,
                                   (const void*)gemm_fp8_dense_kernel};
@@ -910,7 +957,25 @@ hipError_t launch_gemm_fp8_contig(int32_t G, int64_t M, int64_t N, int64_t K, co
   trace_launch(kInfoFp8Contig, dim3((unsigned)grid), "G=%d M=%lld N=%lld K=%lld%s persistent", (int)G, (long long)M,
                (long long)N, (long long)K, valid ? " counts" : "");
   hipLaunchKernelGGL(gemm_fp8_contig_kernel<false>, dim3((unsigned)grid), dim3(kThreads), 0, st, G, M, N, K, a,
-                     sa, b, sb, offsets, valid, d, ldd, nullptr, nullptr);
+                     sa, b, sb, offsets, valid, d, ldd, nullptr, nullptr, nullptr, nullptr, (int64_t)0);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_fp8_combine(int32_t G, int64_t M, int64_t N, int64_t K, const uint8_t* a, const float* sa,
+                                   const uint8_t* b, const float* sb, const int32_t* offsets, const int32_t* valid,
+                                   uint16_t* y, int64_t ldy, const uint8_t* row_info, uint16_t* out, int64_t ldo,
+                                   int num_cus, hipStream_t st) {
+  if (M == 0 || N == 0) return hipSuccess;
+  if (N % 128 != 0 || K % BK != 0 || K / BK > kMaxKb || G < 1 || G > kMaxG || offsets == nullptr ||
+      valid == nullptr)
+    return hipErrorInvalidValue;
+  int64_t grid = (int64_t)num_cus;
+  grid = (grid / kXcds) * kXcds;
+  if (grid < kXcds * kSM) grid = kXcds * kSM;
+  trace_launch(kInfoFp8ContigCombine, dim3((unsigned)grid), "G=%d M=%lld N=%lld K=%lld counts persistent", (int)G,
+               (long long)M, (long long)N, (long long)K);
+  hipLaunchKernelGGL((gemm_fp8_contig_kernel<false, true>), dim3((unsigned)grid), dim3(kThreads), 0, st, G, M, N, K,
+                     a, sa, b, sb, offsets, valid, y, ldy, nullptr, nullptr, row_info, out, ldo);
   return hipGetLastError();
 }
 
@@ -926,7 +991,7 @@ hipError_t launch_gemm_fp8_silu_quantize(int32_t G, int64_t M, int64_t I, int64_
   trace_launch(kInfoFp8ContigSilu, dim3((unsigned)grid), "G=%d M=%lld I=%lld K=%lld%s persistent", (int)G,
                (long long)M, (long long)I, (long long)K, valid ? " counts" : "");
   hipLaunchKernelGGL(gemm_fp8_contig_kernel<true>, dim3((unsigned)grid), dim3(kThreads), 0, st, G, M, 2 * I, K, a,
-                     sa, b, sb, offsets, valid, nullptr, (int64_t)0, q, s);
+                     sa, b, sb, offsets, valid, nullptr, (int64_t)0, q, s, nullptr, nullptr, (int64_t)0);
   return hipGetLastError();
 }
 

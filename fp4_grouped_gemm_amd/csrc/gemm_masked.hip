@@ -179,8 +179,8 @@ gemm_masked_v2_kernel(int G, int64_t M, int64_t N, int64_t K, const uint8_t* __r
   uint16_t* drow = D + ((int64_t)g * M + l16) * ldd + n_base + 4 * q;
 #pragma unroll
   for (int j = 0; j < NT; ++j) {
-    const uint32_t lo = (uint32_t)bf16_bits_rne(acc[j][0]) | ((uint32_t)bf16_bits_rne(acc[j][1]) << 16);
-    const uint32_t hi = (uint32_t)bf16_bits_rne(acc[j][2]) | ((uint32_t)bf16_bits_rne(acc[j][3]) << 16);
+    const uint32_t lo = bf16x2_rne(acc[j][0], acc[j][1]);
+    const uint32_t hi = bf16x2_rne(acc[j][2], acc[j][3]);
     *reinterpret_cast<uint2*>(drow + 16 * j) = make_uint2(lo, hi);
   }
 }
@@ -362,8 +362,8 @@ gemm_masked_fp4_lds_kernel(int G, int64_t M, int64_t N, int64_t K, const uint8_t
   }
   if (l16 >= mm) return;
   uint16_t* drow = D + ((int64_t)g * M + l16) * ldd + n_base + 4 * q;
-  const uint32_t lo = (uint32_t)bf16_bits_rne(acc[0]) | ((uint32_t)bf16_bits_rne(acc[1]) << 16);
-  const uint32_t hi = (uint32_t)bf16_bits_rne(acc[2]) | ((uint32_t)bf16_bits_rne(acc[3]) << 16);
+  const uint32_t lo = bf16x2_rne(acc[0], acc[1]);
+  const uint32_t hi = bf16x2_rne(acc[2], acc[3]);
   *reinterpret_cast<uint2*>(drow) = make_uint2(lo, hi);
 }
 

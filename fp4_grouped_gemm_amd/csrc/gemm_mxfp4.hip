@@ -268,10 +268,8 @@ gemm_mxfp4_kernel(int64_t M, int64_t N, int64_t K, const uint8_t* __restrict__ A
     for (int j = 0; j < kNJ; ++j) {
       const int64_t n = n0 + wn * kWN + 16 * j + 4 * q;
       if (n >= N) continue;                         // N % 16 == 0: a lane's 4 columns are all in or all out
-      const uint32_t lo = (uint32_t)bf16_bits_rne(acc[i][j][0] + bv[j][0]) |
-                          ((uint32_t)bf16_bits_rne(acc[i][j][1] + bv[j][1]) << 16);
-      const uint32_t hi = (uint32_t)bf16_bits_rne(acc[i][j][2] + bv[j][2]) |
-                          ((uint32_t)bf16_bits_rne(acc[i][j][3] + bv[j][3]) << 16);
+      const uint32_t lo = bf16x2_rne(acc[i][j][0] + bv[j][0], acc[i][j][1] + bv[j][1]);
+      const uint32_t hi = bf16x2_rne(acc[i][j][2] + bv[j][2], acc[i][j][3] + bv[j][3]);
       *reinterpret_cast<uint2*>(D + row * ldd + n) = make_uint2(lo, hi);
     }
   }

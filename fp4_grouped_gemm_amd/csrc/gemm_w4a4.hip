@@ -172,10 +172,10 @@ __global__ void __launch_bounds__(256) w4a4_prep_kernel(const uint8_t* __restric
   const int64_t m = m0 + l16;
   if (m >= M) return;
   uint16_t* t = T + m * 32 + 4 * q;
-  *reinterpret_cast<uint2*>(t) = make_uint2((uint32_t)bf16_bits_rne(s0[0]) | ((uint32_t)bf16_bits_rne(s0[1]) << 16),
-                                            (uint32_t)bf16_bits_rne(s0[2]) | ((uint32_t)bf16_bits_rne(s0[3]) << 16));
-  *reinterpret_cast<uint2*>(t + 16) = make_uint2((uint32_t)bf16_bits_rne(s1[0]) | ((uint32_t)bf16_bits_rne(s1[1]) << 16),
-                                                 (uint32_t)bf16_bits_rne(s1[2]) | ((uint32_t)bf16_bits_rne(s1[3]) << 16));
+  *reinterpret_cast<uint2*>(t) = make_uint2(bf16x2_rne(s0[0], s0[1]),
+                                            bf16x2_rne(s0[2], s0[3]));
+  *reinterpret_cast<uint2*>(t + 16) = make_uint2(bf16x2_rne(s1[0], s1[1]),
+                                                 bf16x2_rne(s1[2], s1[3]));
 }
 
 // The fp16 GEMM D = A_h · B_hᵀ (+ T · L_up) (+ bias), bf16 out.  Workgroup tile 256 x 192,
@@ -353,8 +353,8 @@ w4a4_gemm_kernel(int64_t M, int64_t N, int64_t K, const uint16_t* __restrict__ A
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[e] += bf16_to_f32(bias[n + e]);
       }
-      const uint32_t lo = (uint32_t)bf16_bits_rne(v[0]) | ((uint32_t)bf16_bits_rne(v[1]) << 16);
-      const uint32_t hi = (uint32_t)bf16_bits_rne(v[2]) | ((uint32_t)bf16_bits_rne(v[3]) << 16);
+      const uint32_t lo = bf16x2_rne(v[0], v[1]);
+      const uint32_t hi = bf16x2_rne(v[2], v[3]);
       *reinterpret_cast<uint2*>(D + row * ldd + n) = make_uint2(lo, hi);
     }
   }

@@ -439,12 +439,41 @@ hipError_t launch_permute_quantize(const int32_t* ids, int64_t T, int32_t k, int
 // chunks n = 8 * (256 c + tid), four chunks per pass; for each routed slot in
 // increasing j it loads all of its chunks of that row at once, then
 // accumulates them with fp32 FMA (the same order for every column).
+// Routing table of the down GEMM's combine epilogue: per permuted row r < M, the token
+// of its slot and the slot's gate weight when that token has exactly one routed slot
+// (then the row is the token's whole output), else token -1 (padding rows, rows past the
+// routed ones, and rows of tokens with two or more routed slots).
+__global__ void __launch_bounds__(256) combine_rows_kernel(const int32_t* __restrict__ row_to_src,
+                                                            const int32_t* __restrict__ src_to_row,
+                                                            const float* __restrict__ w, int64_t T, int k,
+                                                            int64_t M, uint2* __restrict__ row_info) {
+  const int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (r >= M) return;
+  const int32_t p = row_to_src[r];
+  uint2 e = make_uint2(0xFFFFFFFFu, 0u);
+  if (p >= 0 && (int64_t)p < T * k) {
+    const int64_t t = p / k;
+    int routed = 0;
+    for (int j = 0; j < k; ++j) routed += src_to_row[t * k + j] >= 0;
+    if (routed == 1) e = make_uint2((uint32_t)t, __float_as_uint(w[p]));
+  }
+  row_info[r] = e;
+}
+
+// SKIP_SINGLE: tokens with exactly one routed slot are left alone (the down GEMM's
+// combine epilogue wrote their output rows).
+template <bool SKIP_SINGLE>
 __global__ void __launch_bounds__(256) combine_kernel(const uint16_t* __restrict__ y, int64_t ldy,
                                                        const int32_t* __restrict__ src_to_row,
                                                        const float* __restrict__ w, int64_t T, int k,
                                                        int64_t N, uint16_t* __restrict__ out, int64_t ldo) {
   constexpr int C = 4;
   const int64_t t = blockIdx.x;
+  if constexpr (SKIP_SINGLE) {
+    int routed = 0;
+    for (int j = 0; j < k; ++j) routed += src_to_row[t * k + j] >= 0;
+    if (routed == 1) return;
+  }
   for (int64_t base = 0; base < N; base += C * 2048) {
     float acc[C][8];
 #pragma unroll
@@ -479,7 +508,7 @@ __global__ void __launch_bounds__(256) combine_kernel(const uint16_t* __restrict
         uint32_t o[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          o[i] = (uint32_t)bf16_bits_rne(acc[c][2 * i]) | ((uint32_t)bf16_bits_rne(acc[c][2 * i + 1]) << 16);
+          o[i] = bf16x2_rne(acc[c][2 * i], acc[c][2 * i + 1]);
         *reinterpret_cast<uint4*>(out + t * ldo + n0) = make_uint4(o[0], o[1], o[2], o[3]);
       }
     }
@@ -487,13 +516,37 @@ __global__ void __launch_bounds__(256) combine_kernel(const uint16_t* __restrict
 }
 
 const KernelInfo kInfoCombine = {"combine_kernel", "fgg_moe_combine", 0, 0, 0, 256, 0, 0, 0, 0,
-                                 (const void*)combine_kernel};
+                                 (const void*)combine_kernel<false>};
+const KernelInfo kInfoCombineRest = {"combine_kernel<skip single>", "fgg_moe_down_combine", 0, 0, 0, 256, 0, 0, 0,
+                                     0, (const void*)combine_kernel<true>};
+const KernelInfo kInfoCombineRows = {"combine_rows_kernel", "fgg_moe_down_combine", 0, 0, 0, 256, 0, 0, 0, 0,
+                                     (const void*)combine_rows_kernel};
 
 hipError_t launch_combine(const uint16_t* y, int64_t ldy, const int32_t* src_to_row, const float* w,
                           int64_t T, int32_t k, int64_t N, uint16_t* out, int64_t ldo, hipStream_t st) {
   if (T == 0 || N == 0) return hipSuccess;
   trace_launch(kInfoCombine, dim3((unsigned)T), "T=%lld k=%d N=%lld", (long long)T, (int)k, (long long)N);
-  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)T), dim3(256), 0, st, y, ldy, src_to_row, w, T, (int)k, N, out, ldo);
+  hipLaunchKernelGGL(combine_kernel<false>, dim3((unsigned)T), dim3(256), 0, st, y, ldy, src_to_row, w, T, (int)k, N,
+                     out, ldo);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine_rows(const int32_t* row_to_src, const int32_t* src_to_row, const float* w, int64_t T,
+                               int32_t k, int64_t M, uint8_t* row_info, hipStream_t st) {
+  if (M == 0) return hipSuccess;
+  const int64_t blocks = (M + 255) / 256;
+  trace_launch(kInfoCombineRows, dim3((unsigned)blocks), "M=%lld T=%lld k=%d", (long long)M, (long long)T, (int)k);
+  hipLaunchKernelGGL(combine_rows_kernel, dim3((unsigned)blocks), dim3(256), 0, st, row_to_src, src_to_row, w, T,
+                     (int)k, M, reinterpret_cast<uint2*>(row_info));
+  return hipGetLastError();
+}
+
+hipError_t launch_combine_rest(const uint16_t* y, int64_t ldy, const int32_t* src_to_row, const float* w, int64_t T,
+                               int32_t k, int64_t N, uint16_t* out, int64_t ldo, hipStream_t st) {
+  if (T == 0 || N == 0) return hipSuccess;
+  trace_launch(kInfoCombineRest, dim3((unsigned)T), "T=%lld k=%d N=%lld", (long long)T, (int)k, (long long)N);
+  hipLaunchKernelGGL(combine_kernel<true>, dim3((unsigned)T), dim3(256), 0, st, y, ldy, src_to_row, w, T, (int)k, N,
+                     out, ldo);
   return hipGetLastError();
 }
 

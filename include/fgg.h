@@ -392,6 +392,43 @@ fgg_status fgg_moe_combine(const void* y, int64_t ldy, const int32_t* src_to_row
                            const float* topk_w, int64_t T, int32_t k, int64_t N, void* out,
                            int64_t ldo, void* stream);
 
+/*
+ * fgg_moe_down_combine — the down projection and the gate-weighted combine in one
+ * call.  [MegaMoE] §3 (Mega-MoE: the down GEMM, the weighting and the return to token
+ * order in one pass) and [FP4MoE] §3.2 (results aggregated as they are produced): the
+ * rows of tokens that have exactly one routed slot go from the GEMM's accumulators
+ * straight to the token's output row.
+ *
+ * Result: out is bit-identical to
+ *   fgg_grouped_gemm_scaled(CONTIGUOUS, G, M, N, K, a, a_scales, aq, b, b_scales, bq,
+ *                           offsets, counts, y, ldy)
+ *   fgg_moe_combine(y, ldy, src_to_row, topk_w, T, k, N, out, ldo)
+ * For a routed row r whose token t has exactly one routed slot j, the GEMM's epilogue
+ * writes out[t][n] = bf16_rne(fma(w[t][j], bf16_rne(y_fp32[r][n]), +0)) (the combine's
+ * arithmetic for one slot) and leaves y[r] untouched; every other routed row is written
+ * to y as by fgg_grouped_gemm_scaled, and the combine then handles only the tokens
+ * with zero or at least two routed slots.
+ *   aq = {E4M3,F32,1,128}, bq = {E4M3,F32,128,128}; a, a_scales, b, b_scales, offsets
+ *     and the rules on G, M, N, K as fgg_grouped_gemm_scaled CONTIGUOUS;
+ *   counts [G] (required): the per-expert routed rows from the permute;
+ *   src_to_row [T·k], row_to_src [M] and topk_w [T][k]: the permute's maps (every
+ *     row_to_src entry < T·k or -1) and the gate weights, as fgg_moe_combine;
+ *   y bf16 [M][ldy] (rows of single-slot tokens are not written), out bf16 [T][ldo];
+ *   workspace: ws_bytes >= fgg_moe_down_combine_workspace(M) (16-byte aligned), the
+ *     per-row routing table the call writes and reads (roundup(M, 128) entries of 8 B).
+ * The three kernels (routing table, GEMM, combine of the other tokens) run in order on
+ * `stream`.  Errors as fgg_grouped_gemm_scaled; counts, the maps, the weights, y, out
+ * and the workspace must be non-NULL.
+ */
+fgg_status fgg_moe_down_combine_workspace(int64_t M, size_t* bytes);
+fgg_status fgg_moe_down_combine(int32_t G, int64_t M, int64_t N, int64_t K, const void* a,
+                                const void* a_scales, fgg_qdesc aq, const void* b, const void* b_scales,
+                                fgg_qdesc bq, const int32_t* offsets, const int32_t* counts,
+                                const int32_t* src_to_row, const int32_t* row_to_src,
+                                const float* topk_w, int64_t T, int32_t k, void* y, int64_t ldy,
+                                void* workspace, size_t ws_bytes, void* out, int64_t ldo,
+                                void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -28,7 +28,8 @@ def test_header_declares_the_boundary():
     for n in ["fgg_quantize_blockwise", "fgg_moe_permute", "fgg_moe_permute_workspace", "fgg_moe_permute_quantize",
               "fgg_grouped_gemm_scaled", "fgg_grouped_gemm_silu_quantize",
               "fgg_pack_fp4_weights_bytes", "fgg_pack_fp4_weights",
-              "fgg_scaled_gemm", "fgg_scaled_gemm_workspace", "fgg_moe_combine", "fgg_status_string",
+              "fgg_scaled_gemm", "fgg_scaled_gemm_workspace", "fgg_moe_combine", "fgg_moe_down_combine",
+              "fgg_moe_down_combine_workspace", "fgg_status_string",
               "fgg_last_hip_error", "fgg_set_num_cus"]:
         assert n in names
 
@@ -157,3 +158,13 @@ def test_gemm_and_permute_reject_bad_arguments_on_host():
     assert F(0, 256, 128, 256, g, g, A, g, g, B8, g, None, g, g, None) == 1
     # combine: N not a multiple of 8
     assert lib.fgg_moe_combine(g, 16, g, g, 4, 2, 12, g, 16, None) == 2
+    # fused down GEMM + combine: workspace size, N not a multiple of 128, missing counts,
+    # short workspace, FP4 weights, ldo below N
+    n = ctypes.c_size_t(0)
+    assert lib.fgg_moe_down_combine_workspace(300, ctypes.byref(n)) == 0 and n.value == 384 * 8
+    DC = lib.fgg_moe_down_combine
+    assert DC(2, 256, 200, 256, g, g, A, g, g, B8, g, g, g, g, g, 8, 2, g, 200, g, 4096, g, 200, None) == 2
+    assert DC(2, 256, 256, 256, g, g, A, g, g, B8, g, None, g, g, g, 8, 2, g, 256, g, 4096, g, 256, None) == 1
+    assert DC(2, 256, 256, 256, g, g, A, g, g, B8, g, g, g, g, g, 8, 2, g, 256, g, 1024, g, 256, None) == 1
+    assert DC(2, 256, 256, 256, g, g, A, g, g, B4, g, g, g, g, g, 8, 2, g, 256, g, 4096, g, 256, None) == 2
+    assert DC(2, 256, 256, 256, g, g, A, g, g, B8, g, g, g, g, g, 8, 2, g, 256, g, 4096, g, 128, None) == 1
