@@ -90,7 +90,7 @@ int kernel_table(const KernelInfo* const** out) {
       &kInfoCombineRest,     &kInfoFp8Contig,         &kInfoFp8ContigSilu,  &kInfoFp8ContigCombine,
       &kInfoFp8Dense,        &kInfoMaskedFp4Tiled,    &kInfoMaskedFp4,
       &kInfoMaskedFp8,       &kInfoPackFp4,           &kInfoPackFp4Scales,  &kInfoW4a4Prep,
-      &kInfoW4a4Gemm,        &kInfoMxfp4Gemm,
+      &kInfoW4a4LowRank,     &kInfoW4a4Gemm,         &kInfoMxfp4Gemm,
   };
   *out = table;
   return (int)(sizeof table / sizeof table[0]);

@@ -37,7 +37,7 @@ extern const KernelInfo kInfoQuantE4m3_1x128, kInfoQuantE4m3_128x128, kInfoQuant
     kInfoQuantE2m1E8m0_1x32, kInfoPermuteHist, kInfoPermuteScan, kInfoPermuteScatter, kInfoPermuteGather,
     kInfoPermuteQuantize, kInfoFill, kInfoCombine, kInfoCombineRows, kInfoCombineRest, kInfoFp8Contig,
     kInfoFp8ContigSilu, kInfoFp8ContigCombine, kInfoFp8Dense,
-    kInfoMaskedFp4Tiled, kInfoMaskedFp4, kInfoMaskedFp8, kInfoPackFp4, kInfoPackFp4Scales, kInfoW4a4Prep,
+    kInfoMaskedFp4Tiled, kInfoMaskedFp4, kInfoMaskedFp8, kInfoPackFp4, kInfoPackFp4Scales, kInfoW4a4Prep, kInfoW4a4LowRank,
     kInfoW4a4Gemm, kInfoMxfp4Gemm;
 
 enum class QuantKind { E4M3_1x128, E4M3_128x128, E2M1_1x16, E2M1_E8M0_1x32 };

@@ -60,24 +60,105 @@ __device__ inline void wait_vmcnt() {
 }
 }  // namespace
 
+// The low-rank intermediate T[m][r] = Σ_k X[m][k] · L_down[k][r] (rank 32) for the 16
+// rows of block blk, fp32 accumulate, stored bf16, by the block's W waves.  K is cut
+// into 32-wide chunks, chunk c summed by wave c % W with v_mfma_f32_16x16x32_bf16
+// (first operand: 16 ranks of L_down, second: the 16 X rows; lane (l, q) holds K
+// elements [8q, 8q+8) of row l of each), two rank tiles per wave.  A wave loads the X
+// fragments and L_down slices of kBatch chunks before using any, so that their reads
+// are in flight together (the branch is bound by the latency of these reads, not by
+// their bytes).  L_down is [K][32] (ranks contiguous): each 32-row slice is written
+// transposed into the wave's own LDS area ldt[wave] ([32 ranks][32 k]), from which
+// the rank-major fragments are read (a wave's LDS operations take effect in program
+// order).  The W partial sums are added in wave order through part.
+constexpr int kBatch = 4;
+
+template <int W>
+__device__ inline void lowrank_rows(const uint16_t* __restrict__ X, const uint16_t* __restrict__ Ld,
+                                    uint16_t* __restrict__ T, int64_t M, int64_t K, int64_t blk,
+                                    uint16_t (*ldt)[32 * 32], v4f (*part)[2][64]) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int l16 = lane & 15, q = lane >> 4;
+  const int64_t m0 = blk * 16;
+  int64_t mrow = m0 + l16;
+  if (mrow >= M) mrow = M - 1;               // rows past the end read a valid row; never stored
+  const int nch = (int)(K / 32);             // chunks; wave w takes w, w + W, ...
+  const uint16_t* xr = X + mrow * K + 8 * q;
+  uint16_t* tl = ldt[wave];
+  const int kk = lane >> 1, rb = 16 * (lane & 1);   // the L_down elements this lane moves
+  const bool ld_vec = (reinterpret_cast<uintptr_t>(Ld) & 15u) == 0;
+  v4f acc0 = v4f{0.f, 0.f, 0.f, 0.f}, acc1 = v4f{0.f, 0.f, 0.f, 0.f};
+  for (int c0 = wave; c0 < nch; c0 += W * kBatch) {
+    uint4 xa[kBatch], r0[kBatch], r1[kBatch];
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b) {
+      const int c = c0 + b * W;
+      if (c < nch) {
+        xa[b] = *reinterpret_cast<const uint4*>(xr + (int64_t)c * 32);
+        if (ld_vec) {
+          const uint16_t* src = Ld + ((int64_t)c * 32 + kk) * 32 + rb;   // row 32c + kk, ranks rb .. rb + 15
+          r0[b] = *reinterpret_cast<const uint4*>(src);
+          r1[b] = *reinterpret_cast<const uint4*>(src + 8);
+        }
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b) {
+      const int c = c0 + b * W;
+      if (c >= nch) break;
+      if (ld_vec) {
+        const uint32_t w[8] = {r0[b].x, r0[b].y, r0[b].z, r0[b].w, r1[b].x, r1[b].y, r1[b].z, r1[b].w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          tl[(rb + 2 * e) * 32 + kk] = (uint16_t)(w[e] & 0xFFFFu);
+          tl[(rb + 2 * e + 1) * 32 + kk] = (uint16_t)(w[e] >> 16);
+        }
+      } else {                                        // L_down only 2-byte aligned
+        const uint16_t* src = Ld + ((int64_t)c * 32 + kk) * 32 + rb;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) tl[(rb + e) * 32 + kk] = src[e];
+      }
+      const uint4 la = *reinterpret_cast<const uint4*>(tl + l16 * 32 + 8 * q);
+      const uint4 lb = *reinterpret_cast<const uint4*>(tl + (16 + l16) * 32 + 8 * q);
+      const v8bf xv = __builtin_bit_cast(v8bf, xa[b]);
+      acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, la), xv, acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, lb), xv, acc1, 0, 0, 0);
+    }
+  }
+  part[wave][0][lane] = acc0;
+  part[wave][1][lane] = acc1;
+  __syncthreads();
+  if (wave != 0) return;
+  // lane (l16, q) holds ranks 4q..4q+3 (tile 0) and 16+4q.. (tile 1) of row m0 + l16
+  v4f s0 = part[0][0][lane], s1 = part[0][1][lane];
+#pragma unroll
+  for (int w = 1; w < W; ++w) {
+    const v4f a = part[w][0][lane], b = part[w][1][lane];
+    s0[0] += a[0]; s0[1] += a[1]; s0[2] += a[2]; s0[3] += a[3];
+    s1[0] += b[0]; s1[1] += b[1]; s1[2] += b[2]; s1[3] += b[3];
+  }
+  const int64_t m = m0 + l16;
+  if (m >= M) return;
+  uint16_t* t = T + m * 32 + 4 * q;
+  *reinterpret_cast<uint2*>(t) = make_uint2(bf16x2_rne(s0[0], s0[1]),
+                                            bf16x2_rne(s0[2], s0[3]));
+  *reinterpret_cast<uint2*>(t + 16) = make_uint2(bf16x2_rne(s1[0], s1[1]),
+                                                 bf16x2_rne(s1[2], s1[3]));
+}
+
 // The GEMM's operand preparation and the low-rank branch in one launch, by block
 // ranges, so that the two run side by side:
-//  * blocks [0, M/16) (with the low-rank branch): T[m][r] = Σ_k X[m][k] · L_down[k][r]
-//    (rank 32) for 16 rows each, fp32 accumulate, stored bf16.  Wave w sums K range
-//    [w·K/4, (w+1)·K/4) with v_mfma_f32_16x16x32_bf16 (first operand: 16 ranks of
-//    L_down, second: the 16 X rows; lane (l, q) holds K elements [8q, 8q+8) of row l of
-//    each), two rank tiles per wave.  L_down is [K][32] (ranks contiguous): a wave
-//    loads each 32-row slice of it and writes it transposed into its own LDS area
-//    ([32 ranks][32 k]), from which the rank-major fragments are read (a wave's LDS
-//    operations take effect in program order).  The partial sums are added in wave
-//    order through LDS.
+//  * blocks [0, M/16) (with the low-rank branch): lowrank_rows with four waves;
 //  * the following blocks: packed E2M1 rows with fp32 scales per 16 -> fp16 (x·s
 //    rounded once), for A ([M][K/2] -> [M][K]) and B, 8 elements per item (4 code
 //    bytes in, 16 bytes out), kItems items per thread at a stride of 256 so that each
 //    store instruction writes consecutive 16-byte pieces and every load of a thread is
 //    in flight before its first conversion.
+// Without the dequantization (the MXFP4 form), the low-rank branch runs alone in
+// w4a4_lowrank_kernel, with sixteen waves per 16 rows: more reads in flight per row.
 constexpr int kItems = 4;
 constexpr int kLrWaves = 4;
+constexpr int kLrWavesAlone = 16;
 
 __device__ inline void dequant_items(const uint8_t* __restrict__ q, const float* __restrict__ s, int64_t base,
                                      int64_t n, uint16_t* __restrict__ out) {
@@ -125,59 +206,16 @@ __global__ void __launch_bounds__(256) w4a4_prep_kernel(const uint8_t* __restric
     else dequant_items(qb, sb, (pb - ba) * kPer + threadIdx.x, nb, bh);
     return;
   }
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int l16 = lane & 15, q = lane >> 4;
-  const int64_t m0 = blk * 16;
-  int64_t mrow = m0 + l16;
-  if (mrow >= M) mrow = M - 1;               // rows past the end read a valid row; never stored
-  const int64_t kq = K / kLrWaves;           // a multiple of 32 (K % 128 == 0)
-  const int64_t k_begin = wave * kq, k_end = k_begin + kq;
-  const uint16_t* xr = X + mrow * K + 8 * q;
-  uint16_t* tl = ldt[wave];
-  const int kk = lane >> 1, rb = 16 * (lane & 1);   // the L_down elements this lane moves
-  const bool ld_vec = (reinterpret_cast<uintptr_t>(Ld) & 15u) == 0;
-  v4f acc0 = v4f{0.f, 0.f, 0.f, 0.f}, acc1 = v4f{0.f, 0.f, 0.f, 0.f};
-  for (int64_t k = k_begin; k < k_end; k += 32) {
-    const uint16_t* src = Ld + (k + kk) * 32 + rb;  // row k + kk, ranks rb .. rb + 15
-    const uint4 xa = *reinterpret_cast<const uint4*>(xr + k);
-    if (ld_vec) {
-      const uint4 r0 = *reinterpret_cast<const uint4*>(src);
-      const uint4 r1 = *reinterpret_cast<const uint4*>(src + 8);
-      const uint32_t w[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        tl[(rb + 2 * e) * 32 + kk] = (uint16_t)(w[e] & 0xFFFFu);
-        tl[(rb + 2 * e + 1) * 32 + kk] = (uint16_t)(w[e] >> 16);
-      }
-    } else {                                          // L_down only 2-byte aligned
-#pragma unroll
-      for (int e = 0; e < 16; ++e) tl[(rb + e) * 32 + kk] = src[e];
-    }
-    const uint4 la = *reinterpret_cast<const uint4*>(tl + l16 * 32 + 8 * q);
-    const uint4 lb = *reinterpret_cast<const uint4*>(tl + (16 + l16) * 32 + 8 * q);
-    const v8bf xv = __builtin_bit_cast(v8bf, xa);
-    acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, la), xv, acc0, 0, 0, 0);
-    acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, lb), xv, acc1, 0, 0, 0);
-  }
-  part[wave][0][lane] = acc0;
-  part[wave][1][lane] = acc1;
-  __syncthreads();
-  if (wave != 0) return;
-  // lane (l16, q) holds ranks 4q..4q+3 (tile 0) and 16+4q.. (tile 1) of row m0 + l16
-  v4f s0 = part[0][0][lane], s1 = part[0][1][lane];
-#pragma unroll
-  for (int w = 1; w < kLrWaves; ++w) {
-    const v4f a = part[w][0][lane], b = part[w][1][lane];
-    s0[0] += a[0]; s0[1] += a[1]; s0[2] += a[2]; s0[3] += a[3];
-    s1[0] += b[0]; s1[1] += b[1]; s1[2] += b[2]; s1[3] += b[3];
-  }
-  const int64_t m = m0 + l16;
-  if (m >= M) return;
-  uint16_t* t = T + m * 32 + 4 * q;
-  *reinterpret_cast<uint2*>(t) = make_uint2(bf16x2_rne(s0[0], s0[1]),
-                                            bf16x2_rne(s0[2], s0[3]));
-  *reinterpret_cast<uint2*>(t + 16) = make_uint2(bf16x2_rne(s1[0], s1[1]),
-                                                 bf16x2_rne(s1[2], s1[3]));
+  lowrank_rows<kLrWaves>(X, Ld, T, M, K, blk, ldt, part);
+}
+
+__global__ void __launch_bounds__(64 * kLrWavesAlone) w4a4_lowrank_kernel(const uint16_t* __restrict__ X,
+                                                                          const uint16_t* __restrict__ Ld,
+                                                                          uint16_t* __restrict__ T, int64_t M,
+                                                                          int64_t K) {
+  __shared__ __align__(16) uint16_t ldt[kLrWavesAlone][32 * 32];
+  __shared__ v4f part[kLrWavesAlone][2][64];
+  lowrank_rows<kLrWavesAlone>(X, Ld, T, M, K, blockIdx.x, ldt, part);
 }
 
 // The fp16 GEMM D = A_h · B_hᵀ (+ T · L_up) (+ bias), bf16 out.  Workgroup tile 256 x 192,
@@ -376,18 +414,21 @@ size_t w4a4_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t rank) {
 
 hipError_t launch_lowrank_t(int64_t M, int64_t K, const uint16_t* x_bf16, const uint16_t* l_down, uint16_t* T,
                             hipStream_t st) {
-  // only the low-rank blocks of the preparation kernel (no operand to dequantize)
-  const int64_t lr_blocks = (M + 15) / 16;
-  trace_launch(kInfoW4a4Prep, dim3((unsigned)lr_blocks), "M=%lld K=%lld rank=32 (low-rank blocks only)", (long long)M,
-               (long long)K);
-  hipLaunchKernelGGL(w4a4_prep_kernel, dim3((unsigned)lr_blocks), dim3(256), 0, st, nullptr, nullptr, (int64_t)0,
-                     nullptr, nullptr, nullptr, (int64_t)0, nullptr, x_bf16, l_down, T, M, K, lr_blocks);
+  const int64_t blocks = (M + 15) / 16;
+  trace_launch(kInfoW4a4LowRank, dim3((unsigned)blocks), "M=%lld K=%lld rank=32", (long long)M, (long long)K);
+  hipLaunchKernelGGL(w4a4_lowrank_kernel, dim3((unsigned)blocks), dim3(64 * kLrWavesAlone), 0, st, x_bf16, l_down, T,
+                     M, K);
   return hipGetLastError();
 }
 
 const KernelInfo kInfoW4a4Prep = {"w4a4_prep_kernel", "fgg_scaled_gemm (W4A4)", 16, 32, 0, 256, 0, 0,
                                   kLrWaves * 32 * 32 * 2 + kLrWaves * 2 * 64 * 16,
                                   kLrWaves * 32 * 32 * 2 + kLrWaves * 2 * 64 * 16, (const void*)w4a4_prep_kernel};
+const KernelInfo kInfoW4a4LowRank = {"w4a4_lowrank_kernel", "fgg_scaled_gemm (MXFP4 low-rank branch)", 16, 32, 0,
+                                     64 * kLrWavesAlone, 0, 0,
+                                     kLrWavesAlone * 32 * 32 * 2 + kLrWavesAlone * 2 * 64 * 16,
+                                     kLrWavesAlone * 32 * 32 * 2 + kLrWavesAlone * 2 * 64 * 16,
+                                     (const void*)w4a4_lowrank_kernel};
 const KernelInfo kInfoW4a4Gemm = {"w4a4_gemm_kernel", "fgg_scaled_gemm (W4A4)", w4::BM, w4::BN, w4::BK,
                                   64 * w4::kWaves, w4::kStages, w4::kStageBytes, 0, w4::kStages * w4::kStageBytes,
                                   (const void*)w4a4_gemm_kernel};
