@@ -19,9 +19,10 @@
 // GEMM tile: 256 x 192 per 1024-thread workgroup, four waves per SIMD, each wave 64 x 48
 // outputs (48 fp32 accumulators); two LDS buffers of 64-wide K stages filled by
 // global_load_lds_dwordx4 one stage ahead (details at the kernel).  Measured on MI355X,
-// v_mfma_f32_16x16x32_f16 issues at 2.3-2.4 PFLOP/s from registers (two waves per SIMD,
-// independent accumulators); this GEMM reaches about 1.0 PFLOP/s: with one 256 x 192
-// tile per CU (4096 x 3072) the pipeline fill and the epilogue are not hidden.  The
+// v_mfma_f32_16x16x32_f16 issues at 2.3-2.4 PFLOP/s from registers with constant
+// operands and at 1.6-1.7 PFLOP/s with random ones (the clock drops under the switching
+// load); this GEMM reaches about 1.0 PFLOP/s: with one 256 x 192 tile per CU (4096 x
+// 3072) the pipeline fill and the epilogue are not hidden.  The
 // MXFP4 form (gemm_mxfp4.hip) runs the scaled FP4 MFMA on the codes directly instead.
 #include <algorithm>
 #include <type_traits>
