@@ -213,11 +213,11 @@ __global__ void __launch_bounds__(256) permute_gather_kernel(const int32_t* __re
 
 // Fused quantize + gather: the same outputs as quantizing x to e4m3 with 1x128
 // scales and then gathering the codes (the permute_gather_kernel contract),
-// without writing or re-reading the token-order codes.  One wave per token:
-// lane j < k holds slot j's destination row; a token with no destination
-// below M_cap is not read at all.  The wave walks K in passes of 1024 columns
-// (8 lanes x 16 elements per 128-column group), loading kPB passes before
-// using them, and writes each pass's codes (16 bytes per lane) and scales to
+// without writing or re-reading the token-order codes.  One wave per (token,
+// column batch): lane j < k holds slot j's destination row; a token with no
+// destination below M_cap is not read at all.  The batch is kPermPB passes of
+// 1024 columns (8 lanes x 16 elements per 128-column group), all loaded before
+// the first is used; each pass's codes (16 bytes per lane) and scales go to
 // every destination row.  A second phase zero-fills the padding rows of [0, M_total).
 // Raw bytes of 8 consecutive elements: one 16-byte load for bf16, two for fp32.
 template <bool BF16>
@@ -261,6 +261,13 @@ __device__ inline void unpack_raw8(const RawRow8<BF16>& r, float* f) {
   }
 }
 
+// Columns of one token quantized by one wave: kPermPB passes of 1024 (each lane 16
+// columns per pass), all loaded before the first conversion.  One such item per wave and
+// no loop over items: a wave that looped would wait, at its next item's loads, for its
+// previous stores as well (the vector-memory counter retires loads and stores in order),
+// while a retiring wave's stores drain on their own and its slot takes the next item.
+constexpr int kPermPB = 1;
+
 template <bool BF16>
 __global__ void __launch_bounds__(256) permute_quantize_kernel(const int32_t* __restrict__ offsets, int E, int k,
                                                                 const int32_t* __restrict__ src_to_row,
@@ -269,15 +276,17 @@ __global__ void __launch_bounds__(256) permute_quantize_kernel(const int32_t* __
                                                                 int64_t T, int64_t K,
                                                                 uint8_t* __restrict__ a_out,
                                                                 float* __restrict__ sa_out, int64_t M_cap) {
-  constexpr int kPB = 2;   // passes of 1024 columns loaded together
   const int lane = threadIdx.x & 63, sub = lane & 7;
   const int64_t wave_id = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int64_t nwaves = (int64_t)gridDim.x * 4;
-  for (int64_t t = wave_id; t < T; t += nwaves) {
+  const int64_t nbat = (K + 1024 * kPermPB - 1) / (1024 * kPermPB);
+  // one work item per wave: token t, columns [c0, c0 + 1024 kPermPB)
+  if (wave_id < T * nbat) {
+    const int64_t t = wave_id / nbat, c0 = (wave_id - t * nbat) * (1024 * kPermPB);
     const int32_t dst = lane < k ? src_to_row[t * k + lane] : -1;
     const uint64_t dmask = __ballot(dst >= 0 && dst < M_cap);
-    if (dmask == 0) continue;
-    for (int64_t c0 = 0; c0 < K; c0 += 1024 * kPB) {
+    if (dmask != 0) {
+      constexpr int kPB = kPermPB;
       RawRow8<BF16> raw[kPB][2];
 #pragma unroll
       for (int pb = 0; pb < kPB; ++pb) {
@@ -422,7 +431,9 @@ hipError_t launch_permute_quantize(const int32_t* ids, int64_t T, int32_t k, int
   hipError_t e = launch_permute(ids, T, k, E, align, nullptr, nullptr, K, offsets, counts, src_to_row,
                                 row_to_src, nullptr, nullptr, M_cap, ws, st);
   if (e != hipSuccess || T == 0 || M_cap == 0) return e;
-  const unsigned grid = (unsigned)(num_cus > 0 ? num_cus * 8 : 2048);
+  (void)num_cus;
+  const int64_t nbat = (K + 1024 * kPermPB - 1) / (1024 * kPermPB);
+  const unsigned grid = (unsigned)((T * nbat + 3) / 4);    // one (token, column batch) item per wave
   trace_launch(kInfoPermuteQuantize, dim3(grid), "T=%lld K=%lld %s M_cap=%lld", (long long)T, (long long)K,
                bf16 ? "bf16" : "fp32", (long long)M_cap);
   if (bf16)
