@@ -264,8 +264,9 @@ __device__ inline void unpack_raw8(const RawRow8<BF16>& r, float* f) {
 // Columns of one token quantized by one wave: kPermPB passes of 1024 (each lane 16
 // columns per pass), all loaded before the first conversion.  One such item per wave and
 // no loop over items: a wave that looped would wait, at its next item's loads, for its
-// previous stores as well (the vector-memory counter retires loads and stores in order),
-// while a retiring wave's stores drain on their own and its slot takes the next item.
+// previous stores as well (with loads and stores both outstanding the vector-memory
+// counter gives no order, so the wait is for all of them), while a retiring wave's
+// stores drain on their own and its slot takes the next item.
 constexpr int kPermPB = 1;
 
 template <bool BF16>
