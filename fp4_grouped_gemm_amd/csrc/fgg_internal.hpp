@@ -111,7 +111,7 @@ hipError_t launch_w4a4(int64_t M, int64_t N, int64_t K, const uint8_t* a, const 
                        const uint16_t* l_down, const uint16_t* l_up, int32_t rank,
                        const uint16_t* bias, uint16_t* d, int64_t ldd, void* ws, int num_cus, hipStream_t st);
 
-// T = bf16(X · L_down), rank 32 ([M][32]), by the low-rank blocks of the W4A4 preparation kernel.
+// T = bf16(X · L_down), rank 32 ([M][32]), by w4a4_lowrank_kernel (sixteen waves per 16 rows).
 hipError_t launch_lowrank_t(int64_t M, int64_t K, const uint16_t* x_bf16, const uint16_t* l_down, uint16_t* T,
                             hipStream_t st);
 

@@ -32,8 +32,8 @@
 // dword.  The weight tile is the first operand, so a lane's four results are four
 // consecutive columns of one row (8-byte bf16 stores).
 //
-// The low-rank branch: T = X·L_down ([M][32] bf16, the low-rank blocks of the W4A4
-// operand-preparation kernel) before the GEMM, and one bf16 MFMA step T·L_up (K = 32)
+// The low-rank branch: T = X·L_down ([M][32] bf16, by w4a4_lowrank_kernel in
+// gemm_w4a4.hip) before the GEMM, and one bf16 MFMA step T·L_up (K = 32)
 // into the accumulators of each output tile before the bias is added.
 #include <type_traits>
 

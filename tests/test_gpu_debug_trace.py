@@ -29,6 +29,10 @@ out = fgg.moe_combine(h, p["src_to_row"], torch.ones(256, 1, device=dev))
 y = fgg.scaled_gemm(xq, xs, bq[0], sb[0])
 xq4, xs4 = fgg.quantize_blockwise(x, fgg.Q_E2M1_1x16)
 y4 = fgg.scaled_gemm(xq4, xs4, xq4[:128], xs4[:128], qdesc="w4a4")
+xq5, xe5 = fgg.quantize_blockwise(x, fgg.Q_E2M1_E8M0_1x32)
+ld = (torch.randn(512, 32, device=dev) * 0.01).to(torch.bfloat16)
+lu = (torch.randn(32, 128, device=dev) * 0.01).to(torch.bfloat16)
+y5 = fgg.scaled_gemm(xq5, xe5, xq5[:128], xe5[:128], qdesc="mxfp4", x_bf16=x.to(torch.bfloat16), l_down=ld, l_up=lu)
 torch.cuda.synchronize()
 print("script done")
 """ % ROOT
@@ -42,7 +46,8 @@ def test_debug_trace_names_every_launch():
     for kernel in ("quant_e4m3_1x128_kernel", "quant_e4m3_128x128_kernel", "permute_hist_kernel",
                    "permute_scatter_kernel", "permute_quantize_kernel", "gemm_fp8_contig_kernel<silu>",
                    "gemm_fp8_contig_kernel<plain>", "combine_kernel", "gemm_fp8_dense_kernel",
-                   "quant_e2m1_1x16_kernel", "w4a4_prep_kernel", "w4a4_gemm_kernel"):
+                   "quant_e2m1_1x16_kernel", "w4a4_prep_kernel", "w4a4_gemm_kernel",
+                   "quant_e2m1_e8m0_1x32_kernel", "w4a4_lowrank_kernel", "gemm_mxfp4_kernel"):
         hits = [l for l in lines if l.startswith(f"[fgg] {kernel}:")]
         assert hits, f"no trace line for {kernel}"
         assert "grid=" in hits[0] and "lds=" in hits[0]
