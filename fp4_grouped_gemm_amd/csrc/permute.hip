@@ -434,7 +434,9 @@ hipError_t launch_permute_quantize(const int32_t* ids, int64_t T, int32_t k, int
   if (e != hipSuccess || T == 0 || M_cap == 0) return e;
   (void)num_cus;
   const int64_t nbat = (K + 1024 * kPermPB - 1) / (1024 * kPermPB);
-  const unsigned grid = (unsigned)((T * nbat + 3) / 4);    // one (token, column batch) item per wave
+  const int64_t blocks = (T * nbat + 3) / 4;                // one (token, column batch) item per wave
+  if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+  const unsigned grid = (unsigned)blocks;
   trace_launch(kInfoPermuteQuantize, dim3(grid), "T=%lld K=%lld %s M_cap=%lld", (long long)T, (long long)K,
                bf16 ? "bf16" : "fp32", (long long)M_cap);
   if (bf16)
