@@ -20,8 +20,7 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 
-// e4m3 code of an fp32 value.  Host and device (the host build is used by a
-// CPU unit test of the encoder).
+// e4m3 code of an fp32 value (host and device).
 __host__ __device__ inline uint8_t e4m3_encode(float v) {
   uint32_t bits;
   __builtin_memcpy(&bits, &v, 4);
@@ -173,6 +172,59 @@ __device__ inline void load8(const void* base, int64_t idx, float* f) {
     f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
     f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
   }
+}
+
+// ---------------------------------------------------------------------------
+// gfx950's direct global->LDS loads and the waits the GEMM pipelines count by hand.
+// The LDS destination is M0 (+ 16 or 4 bytes per lane, consecutive lanes consecutive);
+// M0 is saved and restored around the load.  The source is a wave-uniform base (an
+// SGPR pair) plus a per-lane 32-bit offset.  Their completion is counted in vmcnt like
+// any vector-memory load.
+
+// 16 bytes per lane from sbase + voff into LDS at m0 + 16 * lane.
+__device__ inline void dma16(const void* sbase, uint32_t voff, uint32_t lds) {
+  uint32_t save;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(save)
+      : "v"(voff), "s"(sbase), "s"(lds)
+      : "memory");
+}
+
+// 4 bytes per lane from sbase + voff into LDS at m0 + 4 * lane.
+__device__ inline void dma4(const void* sbase, uint32_t voff, uint32_t lds) {
+  uint32_t save;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "global_load_lds_dword %1, %2\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(save)
+      : "v"(voff), "s"(sbase), "s"(lds)
+      : "memory");
+}
+
+// s_waitcnt immediate (gfx9 encoding) for lgkmcnt(0) with vmcnt and expcnt left at their maxima
+constexpr int kLgkmZero = 0xC07F;
+
+template <int N>
+__device__ inline void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+__device__ inline void block_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// A pointer the compiler is told is the same in every lane (it is: built from
+// workgroup-uniform values), so that it can be a DMA instruction's scalar base.
+template <class T>
+__device__ inline T* uniform_ptr(T* p) {
+  const uint64_t v = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (T*)(uintptr_t)(((uint64_t)hi << 32) | lo);
 }
 
 }  // namespace fgg

@@ -99,52 +99,6 @@ static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
 // 16 lanes land on 16 distinct 16-byte slots of the 64 banks (0 conflict cycles).
 __device__ inline int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 
-// 16 bytes per lane from sbase + voff into LDS at m0 + 16 * lane.
-__device__ inline void dma16(const void* sbase, uint32_t voff, uint32_t lds) {
-  uint32_t save;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %3\n\t"
-      "global_load_lds_dwordx4 %1, %2\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(save)
-      : "v"(voff), "s"(sbase), "s"(lds)
-      : "memory");
-}
-
-// 4 bytes per lane from sbase + voff into LDS at m0 + 4 * lane.
-__device__ inline void dma4(const void* sbase, uint32_t voff, uint32_t lds) {
-  uint32_t save;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %3\n\t"
-      "global_load_lds_dword %1, %2\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(save)
-      : "v"(voff), "s"(sbase), "s"(lds)
-      : "memory");
-}
-
-// s_waitcnt immediate (gfx9 encoding) for lgkmcnt(0) with vmcnt and expcnt left at their maxima
-constexpr int kLgkmZero = 0xC07F;
-
-template <int N>
-__device__ inline void wait_vmcnt() {
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-
-__device__ inline void block_barrier() { asm volatile("s_barrier" ::: "memory"); }
-
-// A pointer the compiler is told is the same in every lane (it is: built from
-// workgroup-uniform values), so that it can be a DMA instruction's scalar base.
-template <class T>
-__device__ inline T* uniform_ptr(T* p) {
-  const uint64_t v = (uint64_t)(uintptr_t)p;
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
-  return (T*)(uintptr_t)(((uint64_t)hi << 32) | lo);
-}
-
 // The value of x, hidden from the optimizer: address arithmetic derived from it is
 // computed where it is used (in a tile's epilogue) instead of being hoisted out of
 // the tile loop and held, or spilled, across the K loop.

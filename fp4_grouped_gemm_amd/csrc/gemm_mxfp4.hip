@@ -63,34 +63,6 @@ static_assert(kStages * kStageBytes <= 160 * 1024, "LDS budget");
 static_assert(kStageBytes % 16 == 0, "stage alignment");
 __device__ inline int key(int row) { return (((row >> 2) & 1) * 2) ^ (((row >> 3) & 1) * 3); }
 
-__device__ inline void dma16(const void* sbase, uint32_t voff, uint32_t lds) {
-  uint32_t save;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %3\n\t"
-      "global_load_lds_dwordx4 %1, %2\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(save)
-      : "v"(voff), "s"(sbase), "s"(lds)
-      : "memory");
-}
-
-__device__ inline void dma4(const void* sbase, uint32_t voff, uint32_t lds) {
-  uint32_t save;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %3\n\t"
-      "global_load_lds_dword %1, %2\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(save)
-      : "v"(voff), "s"(sbase), "s"(lds)
-      : "memory");
-}
-
-template <int N>
-__device__ inline void wait_vmcnt() {
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
 }  // namespace mx
 
 __global__ void __launch_bounds__(mx::kThreads, 1)

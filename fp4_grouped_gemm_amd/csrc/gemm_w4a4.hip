@@ -43,22 +43,6 @@ __device__ inline float e2m1_f32(uint32_t nib, float s) {
   return f * s;
 }
 
-__device__ inline void dma16(const void* sbase, uint32_t voff, uint32_t lds) {
-  uint32_t save;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %3\n\t"
-      "global_load_lds_dwordx4 %1, %2\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(save)
-      : "v"(voff), "s"(sbase), "s"(lds)
-      : "memory");
-}
-
-template <int N>
-__device__ inline void wait_vmcnt() {
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
 }  // namespace
 
 // The low-rank intermediate T[m][r] = Σ_k X[m][k] · L_down[k][r] (rank 32) for the 16
